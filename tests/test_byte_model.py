@@ -1,0 +1,45 @@
+"""Pins of the measurement byte model against numbers the pages print."""
+
+import os
+
+import numpy as np
+
+from workloads import byte_model as bm
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    out = {}
+    with open(os.path.join(GOLDEN, "byte_model.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                name, value = line.split()[:2]
+                out[name] = int(value)
+    return out
+
+
+def test_printed_numbers():
+    g = _golden()
+    # one of K or V for one token at 8 kv heads x 128 x 2 bytes is half the
+    # per-token K+V bytes of one layer
+    assert bm.kv_bytes_per_token(1, 8, 128, 2) // 2 == g["single_token_page_bytes"]
+    lens = np.full(64, 4096)
+    assert bm.index_entries(lens, 1) == g["index_entries_page1"]
+    assert bm.index_entries(lens, 16) == g["index_entries_page16"]
+    assert bm.kv_bytes_per_token(32, 8, 128, 2) == g["llama3_8b_bytes_per_token"]
+    assert bm.kv_bytes_per_token(32, 8, 128, 2) * 2048 == g["llama3_8b_2048_tokens"]
+
+
+def test_decode_workload_bytes_and_mixed_flops():
+    # 147,456 tokens x 4096 B is the survey's round figure; check the formula's parts
+    lens = np.full(64, 2304)
+    b = bm.attention_bytes(lens, np.ones(64), 32, 8, 128, 16, 2, 2)
+    kv = 64 * 2304 * 4096
+    assert b == kv + 64 * 32 * 128 * 4 + 64 * 144 * 4 + 64 * 8
+    # one 512-row chunk over 2560 keys: 1,179,904 visible (q, k) pairs per head
+    f = bm.attention_flops([2560], [512], 32, 128)
+    assert f == 4 * 1179904 * 32 * 128
+    # a decode row sees every key
+    assert bm.attention_flops([100], [1], 1, 1) == 400

@@ -1,0 +1,117 @@
+"""Pins of the oracle's split-KV planner (CPU).
+
+The planner is integer work; it is pinned by a hand-worked example
+(tests/golden/plan_worked_example.txt) and by the properties the blog states
+for it ("How Easy Is It to Start Serving LLMs?", Phase 4 §3): every token of
+every request is covered once, pieces never exceed the ideal share, requests
+are placed longest first, each piece goes to the least-loaded queue, and the
+queues end balanced.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+from oracle.plan import split_kv_plan, split_lengths, TILE_TOKENS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    lens, nq, rows = None, None, []
+    with open(os.path.join(GOLDEN, "plan_worked_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("# lengths:"):
+                lens = [int(x) for x in line.split(":")[1].split()]
+            elif line.startswith("# queues:"):
+                nq = int(line.split(":")[1])
+            elif line and not line.startswith("#"):
+                rows.append(tuple(int(x) for x in line.split()))
+    return lens, nq, rows
+
+
+def test_worked_example():
+    lens, nq, rows = _golden()
+    queues = split_kv_plan(lens, nq)
+    got = [(q, r, b, e) for q, items in enumerate(queues) for (r, b, e) in items]
+    assert got == rows
+
+
+def _check_properties(lens, nq):
+    queues = split_kv_plan(lens, nq)
+    assert len(queues) == nq
+    tiles = split_lengths(lens)
+    target = -(-sum(tiles) // nq) if sum(tiles) else 0
+    covered = {r: [] for r in range(len(lens))}
+    for items in queues:
+        load = 0
+        for r, b, e in items:
+            assert 0 <= b < e <= lens[r]
+            assert b % TILE_TOKENS == 0
+            assert e % TILE_TOKENS == 0 or e == lens[r]
+            t = -(-(e - b) // TILE_TOKENS)
+            assert t <= target
+            load += t
+            covered[r].append((b, e))
+        assert load <= target
+    for r, spans in covered.items():
+        spans.sort()
+        pos = 0
+        for b, e in spans:
+            assert b == pos
+            pos = e
+        assert pos == lens[r]
+    return queues, target
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("nq", [1, 3, 16, 256])
+def test_cover_once_pieces_bounded_balanced(seed, nq):
+    rng = np.random.default_rng(seed)
+    lens = list(rng.integers(0, 3000, size=int(rng.integers(1, 70))))
+    _check_properties(lens, nq)
+
+
+def test_longest_first_and_lightest_queue_by_replay():
+    rng = np.random.default_rng(42)
+    lens = list(rng.integers(1, 5000, size=40))
+    nq = 13
+    queues = split_kv_plan(lens, nq)
+    # replay the placement order: requests in longest-first order, pieces of a
+    # request in token order; each placement must have gone to a lightest queue
+    pieces = [(r, b, e, q) for q, items in enumerate(queues) for (r, b, e) in items]
+    order = sorted(range(len(lens)), key=lambda r: (-lens[r], r))
+    rank = {r: i for i, r in enumerate(order)}
+    pieces.sort(key=lambda p: (rank[p[0]], p[1]))
+    loads = [0] * nq
+    seen_in_queue = [0] * nq
+    for r, b, e, q in pieces:
+        assert loads[q] == min(loads)
+        assert q == loads.index(min(loads))  # ties to the lowest index
+        # and a queue's list keeps placement order
+        assert queues[q][seen_in_queue[q]] == (r, b, e)
+        seen_in_queue[q] += 1
+        loads[q] += -(-(e - b) // TILE_TOKENS)
+
+
+def test_balance_on_the_decode_workload():
+    rng = np.random.default_rng([1, 0])
+    lens = list(rng.integers(512, 4096, size=64, endpoint=True))
+    for nq in (256, 512):
+        queues, target = _check_properties(lens, nq)
+        loads = [sum(-(-(e - b) // 16) for _, b, e in q) for q in queues]
+        assert max(loads) <= target
+        assert max(loads) * nq <= 1.05 * sum(split_lengths(lens)) + nq
+        # every request cut at most at queue boundaries: pieces <= queues + requests
+        assert sum(len(q) for q in queues) <= nq + len(lens)
+
+
+def test_empty_and_zero_lengths():
+    assert split_kv_plan([], 4) == [[], [], [], []]
+    assert split_kv_plan([0, 0], 2) == [[], []]
+    q = split_kv_plan([0, 5, 0], 2)
+    assert sum(len(x) for x in q) == 1 and q[0] == [(1, 0, 5)]
+    with pytest.raises(ValueError):
+        split_kv_plan([3], 0)
