@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark: paged decode attention on one MI355X.
+
+One step = one decode step of a Qwen3-4B-shaped model's attention: the
+split-KV plan once on the host, then for each of the 36 layers the write of
+this step's K/V (64 new tokens) and the paged decode over that layer's own
+pool (64 sequences, context uniform in [512, 4096], 32 query / 8 KV heads,
+head dim 128, page 16, bf16).  The plan is made once per step and reused by
+every layer, as the planner's description on "How Easy Is It to Start Serving
+LLMs?" (Phase 4 §3) has it.
+
+Inputs are synthetic: block tables, lengths and slots come from the seeded
+generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
+seeded torch generator per layer and rounded to bf16.  They are resident in
+HBM before timing starts.
+
+Printed: one JSON line.  ``value`` is the step's algorithmic bytes (every
+valid K/V element, q, out, table entries, lengths, and the write's bytes) over
+its wall time, in TB/s.  ``roofline`` covers the dominant call,
+paged_attn_decode, timed with HIP events around every call on its stream.
+``cpu_baseline`` is the fp64 CPU oracle (write + attention of layer 0) timed
+on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_TBS = 8.0
+METRIC = "paged-decode attn achieved HBM TB/s (% of peak) + µs/layer, Qwen3-4B shape"
+LAYERS = 36  # Qwen3-4B decoder layers
+
+CONFIGS = {
+    "decode": dict(config="decode", layout="page16", desc="64 seqs, ctx U[512,4096], 32q/8kv heads, D=128, page 16, bf16 KV"),
+    "long-page1": dict(config="long", layout="page1", desc="16 seqs x 32768, 32q/8kv, D=128, page 1 shuffled, bf16"),
+    "long-page16": dict(config="long", layout="page16", desc="16 seqs x 32768, 32q/8kv, D=128, page 16 shuffled, bf16"),
+    "long-contig": dict(config="long", layout="contig", desc="16 seqs x 32768, 32q/8kv, D=128, contiguous slab, bf16"),
+    "fp8prefix": dict(config="fp8prefix", layout="page16", desc="128 seqs, 4096 shared + 256 private tokens, fp8 E4M3 KV"),
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def build_layers(torch, st, cfg, layers, dev):
+    """Per-layer pools, queries and new K/V on the GPU (seeded)."""
+    import workloads
+
+    hq, hkv, d = 32, 8, 128
+    nb, bs = st["num_blocks"], st["block_size"]
+    B = st["context_lens"].shape[0]
+    fp8 = cfg["config"] == "fp8prefix"
+    out = []
+    for l in range(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(1000 + l)
+        layer = {}
+        if fp8:
+            kc = torch.empty((nb, bs, hkv, d), dtype=torch.uint8, device=dev)
+            vc = torch.empty_like(kc)
+        else:
+            kc = torch.randn((nb, bs, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            vc = torch.randn((nb, bs, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        layer["kc"], layer["vc"] = kc, vc
+        layer["q"] = torch.randn((B, hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        layer["k_new"] = torch.randn((B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        layer["v_new"] = torch.randn((B, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        layer["out"] = torch.empty_like(layer["q"])
+        out.append(layer)
+    return out
+
+
+def fill_fp8(torch, pkv, layers, st, dev):
+    """Fill every fp8 pool by the quantising write from N(0,1) bf16 values."""
+    nb, bs = st["num_blocks"], st["block_size"]
+    hkv, d = 8, 128
+    slots_all = torch.arange(nb * bs, dtype=torch.int32, device=dev)
+    scales = []
+    for i, layer in enumerate(layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(5000 + i)
+        k = torch.randn((nb * bs, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        v = torch.randn((nb * bs, hkv, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ks = float(np.float32(k.float().abs().max().item()) / np.float32(448.0))
+        vs = float(np.float32(v.float().abs().max().item()) / np.float32(448.0))
+        pkv.paged_kv_write(k, v, slots_all, layer["kc"], layer["vc"], ks, vs)
+        scales.append((ks, vs))
+        del k, v
+    return scales
+
+
+def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
+    """The fp64 oracle on layer 0 (write + attention), repeated up to ~budget_s."""
+    import oracle
+    from workloads import byte_model
+
+    def host(t):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    kc, vc = host(layer["kc"]), host(layer["vc"])
+    q, kn, vn = host(layer["q"]), host(layer["k_new"]), host(layer["v_new"])
+    ks, vs = scales
+    B = st["context_lens"].shape[0]
+    cu = np.arange(B + 1, dtype=np.int32)
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        k2, v2 = oracle.kv_write(kc, vc, kv_dtype, kn, vn, "bf16", st["slot_mapping"], ks, vs)
+        out, _ = oracle.paged_attention(q, "bf16", k2, v2, kv_dtype, st["block_tables"], st["context_lens"], cu,
+                                        scale, ks, vs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / reps
+    kvb = 1 if kv_dtype == "fp8" else 2
+    nbytes = byte_model.attention_bytes(st["context_lens"], np.ones(B), 32, 8, 128, st["block_size"], kvb, 2) + \
+        byte_model.write_bytes(B, 8, 128, 2, kvb)
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    cores = len(os.sched_getaffinity(0))
+    return {"value": nbytes / per / 1e12, "unit": "TB/s", "cores": int(blas or cores),
+            "kind": "oracle", "host_cores": cores, "seconds_per_layer_call": per,
+            "sample": f"layer 0 of the step (write of {B} tokens + attention of all {B} sequences), "
+                      f"{reps} repetition(s), fp64 NumPy oracle", "out": out}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--config", default="decode", choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); sharding across GPUs is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_write_amd as pkv
+    import workloads
+    from workloads import byte_model
+
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    st = workloads.structure_only(cfg["config"], cfg["layout"])
+    B = st["context_lens"].shape[0]
+    kv_dtype = "fp8" if cfg["config"] == "fp8prefix" else "bf16"
+    kvb = 1 if kv_dtype == "fp8" else 2
+    log(f"building {args.layers} layers of {args.config}")
+    layers = build_layers(torch, st, cfg, args.layers, dev)
+    scales = [(1.0, 1.0)] * args.layers
+    if kv_dtype == "fp8":
+        scales = fill_fp8(torch, pkv, layers, st, dev)
+    tables = torch.from_numpy(st["block_tables"]).to(dev)
+    ctx = torch.from_numpy(st["context_lens"]).to(dev)
+    slots = torch.from_numpy(st["slot_mapping"]).to(dev)
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    plan = pkv.Plan(st["context_lens"], num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    attn_bytes = byte_model.attention_bytes(st["context_lens"], np.ones(B), 32, 8, 128, st["block_size"], kvb, 2)
+    wr_bytes = byte_model.write_bytes(B, 8, 128, 2, kvb)
+    step_bytes = args.layers * (attn_bytes + wr_bytes)
+
+    n_events = args.steps * args.layers
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    plan_s = []
+
+    def step(timed_index=None):
+        t0 = time.perf_counter()
+        plan.update(st["context_lens"])
+        plan_s.append(time.perf_counter() - t0)
+        for l, layer in enumerate(layers):
+            ks, vs = scales[l]
+            pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
+            if timed_index is not None:
+                ev_a[timed_index * args.layers + l].record(stream)
+            pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan, ks, vs)
+            if timed_index is not None:
+                ev_b[timed_index * args.layers + l].record(stream)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    plan_s.clear()
+    log("timed")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    decode_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    ms_step = wall * 1e3 / args.steps
+    value = step_bytes / (wall / args.steps) / 1e12
+    dec_avg_s = float(decode_ms.mean()) / 1e3
+    achieved = attn_bytes / dec_avg_s / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": kv_dtype,
+        "data": "synthetic: seeded N(0,1) K/V/Q, seeded lengths and shuffled block tables",
+        "config": {
+            "workload": f"{args.config}: {cfg['desc']}; one step = plan + {args.layers} layers x (write + decode)",
+            "num_seqs": int(B),
+            "total_context_tokens": int(st["context_lens"].sum()),
+            "layers": args.layers,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_TBS, 2),
+        "us_per_layer": round(ms_step * 1e3 / args.layers, 3),
+        "decode_call_us": {"mean": round(float(decode_ms.mean()) * 1e3, 3),
+                           "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 3),
+                           "p50": round(float(np.median(decode_ms)) * 1e3, 3),
+                           "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 3)},
+        "plan_us_per_step": round(float(np.median(plan_s)) * 1e6, 2),
+        "plan_us_per_layer": round(float(np.median(plan_s)) * 1e6 / args.layers, 3),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_attn_decode (decode-unit kernel + merge kernel, one call)",
+            "achieved": round(achieved * 1e3, 2),
+            "peak": PEAK_HBM_TBS * 1e3,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_TBS, 4),
+            "bytes_per_launch": int(attn_bytes),
+            "traffic": None,
+        },
+        "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
+                 "merges": int(plan.desc.num_merges), "target_tiles": int(plan.desc.target_tiles)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cb = cpu_baseline(torch, st, layers[0], kv_dtype, scales[0], args.cpu_budget)
+        # parity of layer 0's last timed output against the oracle run above
+        got = layers[0]["out"].float().cpu().numpy().astype(np.float64)
+        cb_out = cb.pop("out")
+        result["parity_max_abs_layer0"] = float(np.max(np.abs(got - cb_out)))
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

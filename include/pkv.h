@@ -1,0 +1,259 @@
+/*
+ * pkv.h - C ABI of a paged-KV attention library for AMD MI355X (gfx950).
+ *
+ * Three operations of an LLM serving step, over a KV cache held as a pool of
+ * fixed-size blocks:
+ *
+ *   paged_kv_write     this step's new K/V rows go to the physical slots a
+ *                      per-token slot list names;
+ *   paged_attn_decode  one query row per sequence attends over its whole
+ *                      context, read in place through a per-sequence block
+ *                      table with an online softmax, long contexts split
+ *                      into pieces that a merge joins back together;
+ *   paged_attn_mixed   the same over a packed batch in which some sequences
+ *                      bring a chunk of several new rows (chunked prefill)
+ *                      and the rest one row each (decode).
+ *
+ * Sources (the pages this library follows):
+ *   "nanoserve" (README): the paged KV cache and per-request block table; the
+ *     packed [T] token batch; one engine step, in which every layer first
+ *     writes this step's K/V through per-token cache slots and then attends
+ *     over the full context through the block table; the paged decode kernel
+ *     with an online softmax over the block table; the split of a mixed step
+ *     into decode rows and prefill chunks.
+ *   "How to design an LLM serving system (a vLLM deep dive)", section
+ *     "PagedAttention": block table, slot_mapping, default block size 16;
+ *     "Two phases and the KV cache": kv bytes per token.
+ *   "How Easy Is It to Start Serving LLMs?", Phase 4 §1 (the block-sparse
+ *     page table: a request reads the pool at the page ids its row lists,
+ *     shared prompt pages are listed by several requests) and §3 (load
+ *     balancing: a host-side plan once per step splits long requests into
+ *     pieces and packs them evenly onto the processors, every layer reuses
+ *     it from a fixed device buffer, and a merge joins the pieces).
+ *
+ * Conventions for every entry point:
+ *   - All pointers are device pointers unless the name ends in _host.  The
+ *     caller owns every buffer; no call allocates or frees memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL is the null stream).  The returned status covers host-side
+ *     argument checks and launch errors only; it is returned before any
+ *     device work runs and nothing is launched when it is not PKV_OK.
+ *   - Index arrays are int32; address arithmetic is 64-bit.
+ *   - Layouts (row-major, innermost last):
+ *       k_cache, v_cache  [num_blocks][block_size][num_kv_heads][head_dim]
+ *       block_tables      [num_seqs][max_blocks_per_seq]
+ *       q, out            [num_tokens][num_q_heads][head_dim]; consecutive
+ *                         tokens of q are q_token_stride elements apart
+ *       k_new, v_new      [num_tokens][num_kv_heads][head_dim]; consecutive
+ *                         tokens new_token_stride elements apart
+ *   - Query head h reads kv head h / (num_q_heads / num_kv_heads).
+ *   - context_lens[s] counts the keys of sequence s after this step's write.
+ *     A chunk of L rows over n keys is aligned at the bottom right: its row i
+ *     sits at position n - L + i and sees keys 0 .. n - L + i.
+ *   - Device-side contents are trusted except where stated: a block id
+ *     outside [0, num_blocks) is never dereferenced; the rows of a sequence
+ *     whose table holds one come out as NaN.
+ *   - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+/* Status codes. */
+#define PKV_OK 0
+#define PKV_ERR_NULL (-1)        /* a required pointer is NULL */
+#define PKV_ERR_SHAPE (-2)       /* inconsistent sizes (heads, lengths, strides) */
+#define PKV_ERR_DTYPE (-3)       /* unknown dtype code */
+#define PKV_ERR_UNSUPPORTED (-4) /* valid but not built: head_dim, group size, dtype pair */
+#define PKV_ERR_WORKSPACE (-5)   /* workspace or host staging buffer too small */
+#define PKV_ERR_PLAN (-6)        /* plan missing, stale or made for other shapes */
+#define PKV_ERR_HIP (-7)         /* a HIP runtime call or kernel launch failed */
+
+/* Storage dtypes. */
+#define PKV_DTYPE_F32 0      /* IEEE binary32 */
+#define PKV_DTYPE_BF16 1     /* bfloat16 */
+#define PKV_DTYPE_FP8_E4M3 2 /* OCP FP8 E4M3 (bias 7, max 448, no inf), one fp32 scale per tensor */
+
+/*
+ * Split-KV plan: a host-side description of work the planner placed in a
+ * workspace.  Filled by paged_attn_plan / paged_attn_plan_host; treat as
+ * opaque.  It stays valid for every call that uses the same workspace, the
+ * same lengths and the same head shape (e.g. all layers of one step).
+ */
+typedef struct pkv_plan {
+    int32_t magic;            /* PKV_PLAN_MAGIC once filled */
+    int32_t num_seqs;
+    int32_t num_tokens;       /* sum of the query rows */
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t num_queues;       /* workgroups of the attention launch */
+    int32_t num_units;        /* pieces of work */
+    int32_t num_merges;       /* groups of rows whose pieces are merged */
+    int32_t num_partial_rows; /* rows of partial results in the workspace */
+    int32_t target_tiles;     /* ideal work per queue, in 16-token tiles */
+    int32_t max_q_len;
+    int64_t off_units;        /* byte offsets inside the workspace */
+    int64_t off_queues;
+    int64_t off_merges;
+    int64_t off_partial_o;
+    int64_t off_partial_lse;
+    int64_t image_bytes;      /* bytes the host image holds (copied to offset 0) */
+    int64_t workspace_bytes;  /* bytes of workspace the plan uses */
+} pkv_plan;
+
+#define PKV_PLAN_MAGIC 0x504b5631 /* "PKV1" */
+
+/* Text of a status code; never NULL. */
+const char* paged_attn_strerror(int status);
+
+/* PKV_ABI_VERSION of the built library. */
+int pkv_abi_version(void);
+
+/*
+ * paged_kv_write - write this step's K/V rows into the block pool by slot.
+ *
+ * For every token t with 0 <= slot_mapping[t] < num_blocks * block_size:
+ *     k_cache viewed as [num_blocks * block_size][num_kv_heads][head_dim]
+ *     row slot_mapping[t] = convert(k_new row t), and likewise for V.
+ * Other slots are not touched; slot < 0 (and a slot past the pool) skips the
+ * token.  convert() is a bit copy when new_dtype == cache_dtype, round to
+ * nearest even for F32 -> BF16, and for a FP8_E4M3 cache the code nearest
+ * to fl32(x / scale) with ties to even, saturating at +-448, NaN -> 0x7F
+ * (k_scale for K, v_scale for V).  Two tokens naming one slot is a caller
+ * error.
+ * ("nanoserve", "One engine step", steps 2-3; "How to design an LLM serving
+ * system", "PagedAttention": slot_mapping tells the kernel where each new
+ * token's K/V goes.)
+ *
+ *   k_new, v_new       device, new_dtype, [num_tokens][num_kv_heads][head_dim]
+ *   new_dtype          F32 or BF16
+ *   new_token_stride   elements between tokens of k_new and v_new
+ *                      (>= num_kv_heads * head_dim)
+ *   slot_mapping       device int32 [num_tokens]
+ *   k_cache, v_cache   device, cache_dtype, the pool
+ *   cache_dtype        F32 (from F32), BF16 (from F32 or BF16), FP8_E4M3
+ *   head_dim           multiple of 8, num_kv_heads * head_dim <= 65536
+ *   k_scale, v_scale   > 0 and finite; used by the FP8 cache only
+ * Returns PKV_OK or an error code; num_tokens == 0 launches nothing.
+ */
+int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                   const int32_t* slot_mapping, int64_t num_tokens, void* k_cache, void* v_cache,
+                   int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, float k_scale, float v_scale, void* stream);
+
+/*
+ * paged_attn_workspace_size - upper bounds of the device workspace and the
+ * host staging image for any plan over at most max_seqs sequences and
+ * max_tokens query rows with the given query heads, head_dim and queues.
+ * num_queues <= 0 asks for the current device's default (a HIP query).
+ */
+int paged_attn_workspace_size(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
+                              int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes);
+
+/* Default number of attention workgroups (queues) on the current device. */
+int paged_attn_default_queues(int32_t* num_queues);
+
+/*
+ * paged_attn_plan_host - the split-KV planner, host memory only.
+ *
+ * Each sequence s brings q_lens[s] query rows (q_lens_host == NULL: one row
+ * each, a decode batch) and context_lens_host[s] keys.  Work is counted in
+ * 16-token tiles; the ideal share per queue is ceil(total tiles /
+ * num_queues); sequences are taken longest first (ties: lower index) and cut
+ * into pieces, each as long as the least-loaded queue (ties: lower index)
+ * can take before it reaches the share, and given to that queue.  Pieces of
+ * a sequence that was cut get rows in the partial-result area and one merge
+ * record.  Query chunks (q_len > 1) are tiled in blocks of rows first and
+ * every (row block, key piece) pair is a unit of its own.
+ * ("How Easy Is It to Start Serving LLMs?", Phase 4 §3.)
+ *
+ * Writes the plan image (units, queue offsets, merge records) into
+ * host_image and describes it in *plan; with host_image == NULL only *plan
+ * is filled (image_bytes tells the size to provide).  No HIP call is made.
+ * Errors: PKV_ERR_SHAPE for a negative length, q_len > context_len,
+ * num_q_heads % num_kv_heads != 0 or num_queues < 1; PKV_ERR_WORKSPACE when
+ * host_bytes < image_bytes.
+ */
+int paged_attn_plan_host(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                         void* host_image, size_t host_bytes, pkv_plan* plan);
+
+/*
+ * paged_attn_plan - paged_attn_plan_host (num_queues <= 0: the device
+ * default) followed by one asynchronous copy of the image into the first
+ * image_bytes of `workspace` on `stream`.  host_staging must stay unchanged
+ * until that copy has run (pinned memory makes it asynchronous; pageable
+ * memory is copied before the call returns).  Every layer of a step reuses
+ * the plan; re-plan when the lengths change.
+ * Errors as paged_attn_plan_host, plus PKV_ERR_WORKSPACE when
+ * workspace_bytes < plan->workspace_bytes and PKV_ERR_HIP.
+ */
+int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                    void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
+                    pkv_plan* plan, void* stream);
+
+/*
+ * paged_attn_decode - one query row per sequence (token s is sequence s).
+ *
+ *   out[s][h][:] = sum_j softmax_j(scale * q[s][h] . K_s[j][g]) V_s[j][g],
+ *   g = h / (num_q_heads / num_kv_heads), j over the n = context_lens[s]
+ *   keys of sequence s, K_s[j] = k_cache[block_tables[s][j / block_size]]
+ *   [j % block_size].  An FP8 cache is read as code * k_scale (K) and
+ *   code * v_scale (V).  Arithmetic in fp32; out has q's dtype (round to
+ *   nearest even).
+ * ("nanoserve", Triton paged-attention decode bullet: every decode reads K/V
+ * straight from the block table with an online softmax; "How Easy Is It to
+ * Start Serving LLMs?", Phase 4 §1 and §3.)
+ *
+ *   out, q            device, q_dtype (F32 or BF16), [num_seqs][num_q_heads][head_dim]
+ *   q_token_stride    elements between tokens of q (>= num_q_heads * head_dim)
+ *   kv_dtype          F32 (q F32), BF16 (q BF16), FP8_E4M3 (q BF16)
+ *   head_dim          64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}
+ *   plan, workspace   from paged_attn_plan with q_lens NULL (or all ones)
+ * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED, PKV_ERR_SHAPE,
+ * PKV_ERR_PLAN (plan made for other shapes or a mixed batch),
+ * PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                      int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_mixed - a packed batch: sequence s owns query rows
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 of q and out (num_tokens rows in all);
+ * row i of its L rows attends causally to keys 0 .. n - L + i of its
+ * n = context_lens[s] keys.  Rows of one-row sequences take the decode
+ * path; chunks take a tiled path whose QK^T and PV products run on the
+ * matrix cores.  Same arguments and errors as paged_attn_decode, with the
+ * plan made from the same q_lens.
+ * ("nanoserve", "Packed batches" and chunked-prefill bullets, and the
+ * benchmark note on splitting each mixed step into decode rows and prefill
+ * chunks; "How to design an LLM serving system", "Latency and scaling
+ * knobs": chunked prefill.)
+ */
+int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                     const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
+                     float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -44,8 +44,10 @@ def kv_write(
     slot_mapping: np.ndarray,
     k_scale: float = 1.0,
     v_scale: float = 1.0,
+    inplace: bool = False,
 ):
-    """Return copies of the caches after writing this step's K/V by slot.
+    """Return the caches after writing this step's K/V by slot (copies unless
+    ``inplace``, which writes into the given arrays).
 
     ``cache.reshape(num_blocks * block_size, H_kv, D)[slot[t]] = enc(new[t])``
     for every token with ``0 <= slot[t] < num_blocks * block_size``; every
@@ -54,8 +56,8 @@ def kv_write(
     ``enc`` converts the stored new values into the cache dtype (bit copy when
     they match, fp8 quantisation with the per-tensor scale otherwise).
     """
-    kc = np.array(k_cache, copy=True)
-    vc = np.array(v_cache, copy=True)
+    kc = k_cache if inplace else np.array(k_cache, copy=True)
+    vc = v_cache if inplace else np.array(v_cache, copy=True)
     nb, bs, hkv, d = kc.shape
     flat_k = kc.reshape(nb * bs, hkv, d)
     flat_v = vc.reshape(nb * bs, hkv, d)

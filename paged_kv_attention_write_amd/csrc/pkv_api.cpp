@@ -1,0 +1,250 @@
+// C ABI: argument checks, the plan upload and kernel launches.  Every check
+// runs on the host before anything is launched; a failing check returns a
+// negative status and leaves device memory untouched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pkv_attention.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using namespace pkv;
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Persistent attention workgroups per compute unit (two 8-wave workgroups
+// fill 16 wave slots of a CU at <= 128 VGPRs per lane).
+constexpr int kQueuesPerCU = 2;
+
+bool dtype_ok(int32_t dt) { return dt == PKV_DTYPE_F32 || dt == PKV_DTYPE_BF16 || dt == PKV_DTYPE_FP8_E4M3; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool attn_pair_ok(int32_t q_dtype, int32_t kv_dtype) {
+    return (q_dtype == PKV_DTYPE_F32 && kv_dtype == PKV_DTYPE_F32) ||
+           (q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_BF16) ||
+           (q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_FP8_E4M3);
+}
+
+// Checks shared by decode and mixed.  `rows` = query rows in q/out.
+int check_attention(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                    const void* v_cache, int32_t kv_dtype, const int32_t* block_tables, int32_t max_blocks,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t rows, int32_t hq, int32_t hkv,
+                    int32_t d, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
+                    float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes) {
+    if (!dtype_ok(q_dtype) || !dtype_ok(kv_dtype) || q_dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_DTYPE;
+    if (plan == nullptr) return PKV_ERR_NULL;
+    if (num_seqs < 0 || rows < 0 || hq < 1 || hkv < 1 || hq % hkv != 0 || block_size < 1 || num_blocks < 1 ||
+        max_blocks < 1)
+        return PKV_ERR_SHAPE;
+    if (d != 64 && d != 128) return PKV_ERR_UNSUPPORTED;
+    const int32_t group = hq / hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PKV_ERR_UNSUPPORTED;
+    if (!attn_pair_ok(q_dtype, kv_dtype)) return PKV_ERR_UNSUPPORTED;
+    if (q_token_stride < static_cast<int64_t>(hq) * d) return PKV_ERR_SHAPE;
+    if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+    if (kv_dtype == PKV_DTYPE_FP8_E4M3 &&
+        (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PKV_ERR_SHAPE;
+    if (plan->magic != PKV_PLAN_MAGIC || plan->num_seqs != num_seqs || plan->num_tokens != rows ||
+        plan->num_q_heads != hq || plan->num_kv_heads != hkv || plan->head_dim != d)
+        return PKV_ERR_PLAN;
+    if (rows == 0) return PKV_OK;
+    if (out == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
+        context_lens == nullptr || workspace == nullptr)
+        return PKV_ERR_NULL;
+    if (workspace_bytes < static_cast<size_t>(plan->workspace_bytes)) return PKV_ERR_WORKSPACE;
+    // vector loads: every lane reads D/16 contiguous elements
+    const size_t qb = static_cast<size_t>(dt_bytes(q_dtype));
+    const size_t lane_q = static_cast<size_t>(d / 16) * qb;
+    const size_t lane_kv = static_cast<size_t>(d / 16) * static_cast<size_t>(dt_bytes(kv_dtype));
+    const size_t qa = lane_q >= 16 ? 16 : lane_q;
+    const size_t kva = lane_kv >= 16 ? 16 : lane_kv;
+    if (!aligned(q, qa) || (static_cast<size_t>(q_token_stride) * qb) % qa != 0 || !aligned(out, qa) ||
+        !aligned(k_cache, kva) || !aligned(v_cache, kva) || !aligned(workspace, kAlign))
+        return PKV_ERR_SHAPE;
+    return PKV_OK;
+}
+
+AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void* k_cache, const void* v_cache,
+                   int32_t kv_dtype, const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                   int32_t hq, int32_t hkv, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
+                   float v_scale, const pkv_plan* plan, void* workspace) {
+    char* ws = static_cast<char*>(workspace);
+    const bool fp8 = kv_dtype == PKV_DTYPE_FP8_E4M3;
+    AttnArgs a;
+    a.out = out;
+    a.q = q;
+    a.q_stride = q_token_stride;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.max_blocks = max_blocks;
+    a.context_lens = context_lens;
+    a.hq = hq;
+    a.hkv = hkv;
+    a.num_blocks = num_blocks;
+    a.block_size = block_size;
+    a.qk_scale = scale * (fp8 ? k_scale : 1.f) * kLog2e;
+    a.v_scale = fp8 ? v_scale : 1.f;
+    a.units = reinterpret_cast<const Unit*>(ws + plan->off_units);
+    a.queue_off = reinterpret_cast<const int32_t*>(ws + plan->off_queues);
+    a.partial_o = reinterpret_cast<float*>(ws + plan->off_partial_o);
+    a.partial_lse = reinterpret_cast<float*>(ws + plan->off_partial_lse);
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_attn_strerror(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_SHAPE: return "inconsistent sizes, strides, lengths or alignment";
+        case PKV_ERR_DTYPE: return "unknown dtype code";
+        case PKV_ERR_UNSUPPORTED: return "unsupported head_dim, group size or dtype pair";
+        case PKV_ERR_WORKSPACE: return "workspace or host staging buffer too small";
+        case PKV_ERR_PLAN: return "plan missing, stale or made for other shapes";
+        case PKV_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                   const int32_t* slot_mapping, int64_t num_tokens, void* k_cache, void* v_cache,
+                   int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, float k_scale, float v_scale, void* stream) {
+    if (!dtype_ok(new_dtype) || !dtype_ok(cache_dtype) || new_dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_DTYPE;
+    const bool pair = (new_dtype == cache_dtype) || (new_dtype == PKV_DTYPE_F32 && cache_dtype == PKV_DTYPE_BF16) ||
+                      cache_dtype == PKV_DTYPE_FP8_E4M3;
+    if (!pair) return PKV_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 8 ||
+        head_dim % 8 != 0 || static_cast<int64_t>(num_kv_heads) * head_dim > 65536)
+        return PKV_ERR_SHAPE;
+    const int64_t hd = static_cast<int64_t>(num_kv_heads) * head_dim;
+    if (new_token_stride < hd || new_token_stride % 8 != 0) return PKV_ERR_SHAPE;
+    if (cache_dtype == PKV_DTYPE_FP8_E4M3 &&
+        (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
+        return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
+    const size_t in_align = new_dtype == PKV_DTYPE_F32 ? 16 : 16;
+    const size_t out_align = cache_dtype == PKV_DTYPE_FP8_E4M3 ? 8 : 16;
+    if (!aligned(k_new, in_align) || !aligned(v_new, in_align) || !aligned(k_cache, out_align) ||
+        !aligned(v_cache, out_align))
+        return PKV_ERR_SHAPE;
+    if (num_blocks > INT64_MAX / block_size) return PKV_ERR_SHAPE;
+    return launch_kv_write(k_new, v_new, new_dtype, new_token_stride, slot_mapping, num_tokens, k_cache, v_cache,
+                           cache_dtype, num_blocks * block_size, static_cast<int32_t>(hd), k_scale, v_scale,
+                           stream);
+}
+
+int paged_attn_default_queues(int32_t* num_queues) {
+    if (num_queues == nullptr) return PKV_ERR_NULL;
+    int dev = 0;
+    int cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return PKV_ERR_HIP;
+    *num_queues = cus * kQueuesPerCU;
+    return PKV_OK;
+}
+
+int paged_attn_workspace_size(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
+                              int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes) {
+    if (workspace_bytes == nullptr && host_bytes == nullptr) return PKV_ERR_NULL;
+    if (max_seqs < 0 || max_tokens < 0 || num_q_heads < 1 || head_dim < 1) return PKV_ERR_SHAPE;
+    if (num_queues <= 0) {
+        const int st = paged_attn_default_queues(&num_queues);
+        if (st != PKV_OK) return st;
+    }
+    plan_bounds(max_seqs, max_tokens, num_q_heads, head_dim, num_queues, workspace_bytes, host_bytes);
+    return PKV_OK;
+}
+
+int paged_attn_plan_host(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                         void* host_image, size_t host_bytes, pkv_plan* plan) {
+    return plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
+                     host_image, host_bytes, plan);
+}
+
+int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                    void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
+                    pkv_plan* plan, void* stream) {
+    if (plan == nullptr || host_staging == nullptr || workspace == nullptr) return PKV_ERR_NULL;
+    if (num_queues <= 0) {
+        const int st = paged_attn_default_queues(&num_queues);
+        if (st != PKV_OK) return st;
+    }
+    int st = plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
+                       host_staging, host_staging_bytes, plan);
+    if (st != PKV_OK) return st;
+    if (workspace_bytes < static_cast<size_t>(plan->workspace_bytes) || !aligned(workspace, kAlign)) {
+        plan->magic = 0;
+        return PKV_ERR_WORKSPACE;
+    }
+    if (hipMemcpyAsync(workspace, host_staging, static_cast<size_t>(plan->image_bytes), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(stream)) != hipSuccess) {
+        plan->magic = 0;
+        return PKV_ERR_HIP;
+    }
+    return PKV_OK;
+}
+
+int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                      int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                             max_blocks_per_seq, context_lens, num_seqs, num_seqs, num_q_heads, num_kv_heads,
+                             head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan, workspace,
+                             workspace_bytes);
+    if (st != PKV_OK) return st;
+    if (plan->max_q_len > 1) return PKV_ERR_PLAN;
+    if (num_seqs == 0) return PKV_OK;
+    const AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                                 max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, num_blocks, block_size,
+                                 scale, k_scale, v_scale, plan, workspace);
+    st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+    if (st != PKV_OK) return st;
+    const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
+    return launch_merge(a, merges, plan->num_merges, q_dtype, head_dim, stream);
+}
+
+int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                     const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
+                     float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                             max_blocks_per_seq, context_lens, num_seqs, num_tokens, num_q_heads, num_kv_heads,
+                             head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan, workspace,
+                             workspace_bytes);
+    if (st != PKV_OK) return st;
+    if (num_tokens == 0) return PKV_OK;
+    if (cu_seqlens == nullptr) return PKV_ERR_NULL;
+    const AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                                 max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, num_blocks, block_size,
+                                 scale, k_scale, v_scale, plan, workspace);
+    if (plan->max_q_len <= 1)
+        st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+    else
+        st = launch_mixed(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+    if (st != PKV_OK) return st;
+    const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
+    return launch_merge(a, merges, plan->num_merges, q_dtype, head_dim, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Arguments and launchers of the attention kernels (decode, mixed, merge).
+#pragma once
+
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int dt_bytes(int dt) { return dt == PKV_DTYPE_F32 ? 4 : (dt == PKV_DTYPE_BF16 ? 2 : 1); }
+
+struct AttnArgs {
+    void* out;                    // [T][hq][D], q's dtype, contiguous
+    const void* q;                // [T][hq][D] with token stride q_stride
+    int64_t q_stride;             // elements
+    const void* k_cache;          // [num_blocks][block_size][hkv][D]
+    const void* v_cache;
+    const int32_t* block_tables;  // [B][max_blocks]
+    int32_t max_blocks;
+    const int32_t* context_lens;  // [B]
+    int32_t hq;
+    int32_t hkv;
+    int64_t num_blocks;
+    int32_t block_size;
+    float qk_scale;               // scale * k_scale * log2(e): scores in log2 units
+    float v_scale;                // applied to the final output
+    const Unit* units;
+    const int32_t* queue_off;
+    float* partial_o;             // [rows][hq][D]
+    float* partial_lse;           // [rows][hq], log2 units
+};
+
+// Store EPL fp32 values as the output dtype (bf16: round to nearest even).
+template <int QDT, int EPL>
+__device__ __forceinline__ void store_out(char* dst, const float (&o)[EPL]) {
+    if constexpr (QDT == PKV_DTYPE_F32) {
+        Words<EPL> w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) w.w[e] = __float_as_uint(o[e]);
+        store_words<EPL>(dst, w);
+    } else {
+        Words<EPL / 2> w;
+#pragma unroll
+        for (int j = 0; j < EPL / 2; ++j) w.w[j] = f32_to_bf16_rne(o[2 * j]) | (f32_to_bf16_rne(o[2 * j + 1]) << 16);
+        store_words<EPL / 2>(dst, w);
+    }
+}
+
+int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
+                  void* stream);
+int launch_mixed(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
+                 void* stream);
+int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int q_dtype, int head_dim, void* stream);
+int launch_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t stride_elems,
+                    const int32_t* slots, int64_t T, void* kc, void* vc, int32_t cache_dtype, int64_t num_slots,
+                    int32_t hd, float ks, float vs, void* stream);
+
+}  // namespace pkv

@@ -1,0 +1,68 @@
+// Host-side structures shared by the planner, the C-ABI layer and the kernel
+// launchers.  The device reads the same records from the workspace.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// Work is counted in tiles of this many keys; piece boundaries inside a
+// sequence fall on tile boundaries.
+constexpr int kTileTokens = 16;
+// Rows of a query chunk handled by one prefill unit.
+constexpr int kPrefillRows = 64;
+// Key pieces of a prefill row block: at least this long, at most this many.
+constexpr int kPrefillPieceMin = 512;
+constexpr int kPrefillMaxPieces = 8;
+// Cost of a prefill unit in decode tiles: one tile of decode work (16 keys of
+// 8 kv heads x 128 dims in bf16, 64 KiB) takes as long as this many flops of
+// matrix-core work at the rates the kernels reach (HBM ~6 TB/s against
+// ~1.2 PFLOP/s of bf16 MFMA).
+constexpr double kFlopsPerTile = 13.0e6;
+
+// Alignment of the sections of the workspace.
+constexpr size_t kAlign = 256;
+
+enum UnitKind : int32_t { kUnitDecode = 0, kUnitPrefill = 1 };
+
+// One piece of work: query rows [row0, row0 + nrows) of sequence `seq` (rows
+// are packed token indices) against keys [kv_begin, kv_end).  Row r of the
+// unit sits at position pos0 + r.  prow >= 0: write the normalised partial
+// result of row r to partial row prow + r; prow < 0: write the output.
+struct Unit {
+    int32_t seq;
+    int32_t kv_begin;
+    int32_t kv_end;
+    int32_t row0;
+    int32_t nrows;
+    int32_t pos0;
+    int32_t prow;
+    int32_t kind;
+};
+static_assert(sizeof(Unit) == 32, "unit record is 32 bytes");
+
+// Rows [row0, row0 + nrows) whose `parts` partial results sit at partial
+// rows prow0 + c * nrows + r, c = 0 .. parts-1, in key order.
+struct Merge {
+    int32_t row0;
+    int32_t nrows;
+    int32_t prow0;
+    int32_t parts;
+};
+static_assert(sizeof(Merge) == 16, "merge record is 16 bytes");
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Planner (pkv_plan.cpp).  Pure host code.
+int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
+              size_t host_bytes, pkv_plan* plan);
+
+// Upper bounds used by paged_attn_workspace_size.
+void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
+                 int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes);
+
+}  // namespace pkv

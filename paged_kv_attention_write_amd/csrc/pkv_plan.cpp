@@ -1,0 +1,245 @@
+// Split-KV planner: host code, once per step, reused by every layer.
+//
+// "How Easy Is It to Start Serving LLMs?", Phase 4 §3 (load balancing): the
+// ideal work per processor is the total over the processor count; requests
+// are taken longest first and cut into pieces no longer than that share;
+// every piece goes to the least-loaded queue.  Here work is counted in
+// 16-token tiles, the share is rounded up to whole tiles, and each piece is
+// cut to what the least-loaded queue can still take before it reaches the
+// share, so queues end within one tile of each other and a request is cut
+// only where a queue fills up (at most queues + requests pieces in all).
+//
+// Query chunks (more than one new row) are split into blocks of rows and key
+// pieces first; each (row block, key piece) pair is one whole unit whose cost
+// is its matrix-core work expressed in tiles, and these units are placed
+// before the decode requests, largest first.
+#include <algorithm>
+#include <cstring>
+#include <queue>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+struct QueueHeap {
+    // (load, index) min-heap: the lightest queue, ties to the lowest index.
+    using Item = std::pair<int64_t, int32_t>;
+    std::priority_queue<Item, std::vector<Item>, std::greater<Item>> heap;
+    explicit QueueHeap(int32_t n) {
+        std::vector<Item> init;
+        init.reserve(n);
+        for (int32_t i = 0; i < n; ++i) init.emplace_back(0, i);
+        heap = decltype(heap)(std::greater<Item>(), std::move(init));
+    }
+    Item pop() {
+        Item it = heap.top();
+        heap.pop();
+        return it;
+    }
+    void push(int64_t load, int32_t q) { heap.emplace(load, q); }
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct PrefillPiece {
+    Unit unit;
+    int64_t cost;   // tiles
+    int32_t order;  // creation order, breaks cost ties
+};
+
+}  // namespace
+
+int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
+              size_t host_bytes, pkv_plan* plan) {
+    if (plan == nullptr || (num_seqs > 0 && ctx == nullptr)) return PKV_ERR_NULL;
+    std::memset(plan, 0, sizeof(*plan));
+    if (num_seqs < 0 || num_queues < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
+        num_q_heads % num_kv_heads != 0)
+        return PKV_ERR_SHAPE;
+
+    // Validate lengths and collect packed row offsets.
+    std::vector<int32_t> row0(static_cast<size_t>(num_seqs) + 1, 0);
+    int64_t rows = 0;
+    int32_t max_q = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = ctx[s];
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (n < 0 || L < 0 || L > n) return PKV_ERR_SHAPE;
+        row0[s] = static_cast<int32_t>(rows);
+        rows += L;
+        if (rows > INT32_MAX) return PKV_ERR_SHAPE;
+        max_q = std::max(max_q, L);
+    }
+    row0[num_seqs] = static_cast<int32_t>(rows);
+
+    const int64_t hd = static_cast<int64_t>(num_q_heads) * head_dim;
+
+    // Prefill units: row blocks x key pieces of every chunk.
+    std::vector<PrefillPiece> prefill;
+    std::vector<Merge> merges;
+    int64_t partial_rows = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = ctx[s];
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (L <= 1) continue;
+        for (int32_t r0 = 0; r0 < L; r0 += kPrefillRows) {
+            const int32_t r1 = std::min(L, r0 + kPrefillRows);
+            const int32_t nr = r1 - r0;
+            const int32_t extent = n - L + r1;  // keys the last row of the block sees
+            int64_t piece = std::max<int64_t>(kPrefillPieceMin, ceil_div(extent, kPrefillMaxPieces));
+            piece = ceil_div(piece, kTileTokens) * kTileTokens;
+            const int32_t parts = static_cast<int32_t>(ceil_div(extent, piece));
+            const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
+            if (parts > 1) {
+                merges.push_back(Merge{row0[s] + r0, nr, prow0, parts});
+                partial_rows += static_cast<int64_t>(parts) * nr;
+            }
+            for (int32_t c = 0; c < parts; ++c) {
+                const int32_t kb = static_cast<int32_t>(c * piece);
+                const int32_t ke = static_cast<int32_t>(std::min<int64_t>(extent, kb + piece));
+                // visible (row, key) pairs of the unit
+                int64_t pairs = 0;
+                for (int32_t r = r0; r < r1; ++r) {
+                    const int64_t last = static_cast<int64_t>(n) - L + r;  // position of row r
+                    pairs += std::max<int64_t>(0, std::min<int64_t>(ke - 1, last) - kb + 1);
+                }
+                const double flops = 4.0 * static_cast<double>(pairs) * static_cast<double>(hd);
+                const int64_t cost = std::max<int64_t>(1, static_cast<int64_t>(flops / kFlopsPerTile + 0.5));
+                Unit u{s, kb, ke, row0[s] + r0, nr, n - L + r0, parts > 1 ? prow0 + c * nr : -1,
+                       kUnitPrefill};
+                prefill.push_back(PrefillPiece{u, cost, static_cast<int32_t>(prefill.size())});
+            }
+        }
+    }
+
+    // Total work and the share per queue.
+    int64_t total = 0;
+    for (const auto& p : prefill) total += p.cost;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (L == 1) total += ceil_div(ctx[s], kTileTokens);
+    }
+    const int64_t target = total > 0 ? ceil_div(total, num_queues) : 0;
+
+    std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
+    QueueHeap heap(num_queues);
+
+    // Whole prefill units, largest first.
+    std::stable_sort(prefill.begin(), prefill.end(), [](const PrefillPiece& a, const PrefillPiece& b) {
+        return a.cost > b.cost;
+    });
+    for (const auto& p : prefill) {
+        auto [load, q] = heap.pop();
+        queues[q].push_back(p.unit);
+        heap.push(load + p.cost, q);
+    }
+
+    // Decode requests, longest first, cut to fill the lightest queue.
+    std::vector<int32_t> order;
+    for (int32_t s = 0; s < num_seqs; ++s)
+        if ((q_lens ? q_lens[s] : 1) == 1 && ctx[s] > 0) order.push_back(s);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return ctx[a] > ctx[b]; });
+    std::vector<std::pair<int32_t, size_t>> placed;  // (queue, index) of the pieces of one request
+    for (int32_t s : order) {
+        const int32_t n = ctx[s];
+        int64_t remaining = ceil_div(n, kTileTokens);
+        int64_t first = 0;
+        placed.clear();
+        while (remaining > 0) {
+            auto [load, q] = heap.pop();
+            const int64_t take = std::min(remaining, target - load);
+            const int32_t kb = static_cast<int32_t>(first * kTileTokens);
+            const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, (first + take) * kTileTokens));
+            queues[q].push_back(Unit{s, kb, ke, row0[s], 1, n - 1, -1, kUnitDecode});
+            placed.emplace_back(q, queues[q].size() - 1);
+            heap.push(load + take, q);
+            remaining -= take;
+            first += take;
+        }
+        if (placed.size() > 1) {
+            const int32_t prow0 = static_cast<int32_t>(partial_rows);
+            for (size_t c = 0; c < placed.size(); ++c)
+                queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c);
+            merges.push_back(Merge{row0[s], 1, prow0, static_cast<int32_t>(placed.size())});
+            partial_rows += static_cast<int64_t>(placed.size());
+        }
+    }
+
+    int64_t num_units = 0;
+    for (const auto& q : queues) num_units += static_cast<int64_t>(q.size());
+    if (num_units > INT32_MAX || partial_rows > INT32_MAX) return PKV_ERR_SHAPE;
+
+    // Image: [units][queue offsets][merges], then the partial results.
+    const size_t units_bytes = align_up(static_cast<size_t>(num_units) * sizeof(Unit));
+    const size_t queues_bytes = align_up((static_cast<size_t>(num_queues) + 1) * sizeof(int32_t));
+    const size_t merges_bytes = align_up(merges.size() * sizeof(Merge));
+    const size_t image = units_bytes + queues_bytes + merges_bytes;
+    const size_t po_bytes = align_up(static_cast<size_t>(partial_rows) * static_cast<size_t>(hd) * sizeof(float));
+    const size_t pl_bytes =
+        align_up(static_cast<size_t>(partial_rows) * static_cast<size_t>(num_q_heads) * sizeof(float));
+
+    plan->num_seqs = num_seqs;
+    plan->num_tokens = static_cast<int32_t>(rows);
+    plan->num_q_heads = num_q_heads;
+    plan->num_kv_heads = num_kv_heads;
+    plan->head_dim = head_dim;
+    plan->num_queues = num_queues;
+    plan->num_units = static_cast<int32_t>(num_units);
+    plan->num_merges = static_cast<int32_t>(merges.size());
+    plan->num_partial_rows = static_cast<int32_t>(partial_rows);
+    plan->target_tiles = static_cast<int32_t>(std::min<int64_t>(target, INT32_MAX));
+    plan->max_q_len = max_q;
+    plan->off_units = 0;
+    plan->off_queues = static_cast<int64_t>(units_bytes);
+    plan->off_merges = static_cast<int64_t>(units_bytes + queues_bytes);
+    plan->off_partial_o = static_cast<int64_t>(image);
+    plan->off_partial_lse = static_cast<int64_t>(image + po_bytes);
+    plan->image_bytes = static_cast<int64_t>(image);
+    plan->workspace_bytes = static_cast<int64_t>(image + po_bytes + pl_bytes);
+
+    if (host_image == nullptr) {
+        plan->magic = PKV_PLAN_MAGIC;
+        return PKV_OK;
+    }
+    if (host_bytes < image) return PKV_ERR_WORKSPACE;
+    char* base = static_cast<char*>(host_image);
+    std::memset(base, 0, image);
+    Unit* u = reinterpret_cast<Unit*>(base);
+    int32_t* qoff = reinterpret_cast<int32_t*>(base + units_bytes);
+    int32_t cursor = 0;
+    for (int32_t q = 0; q < num_queues; ++q) {
+        qoff[q] = cursor;
+        for (const Unit& x : queues[q]) u[cursor++] = x;
+    }
+    qoff[num_queues] = cursor;
+    if (!merges.empty())
+        std::memcpy(base + units_bytes + queues_bytes, merges.data(), merges.size() * sizeof(Merge));
+    plan->magic = PKV_PLAN_MAGIC;
+    return PKV_OK;
+}
+
+void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
+                 int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes) {
+    const int64_t seqs = std::max<int32_t>(max_seqs, 0);
+    const int64_t toks = std::max<int32_t>(max_tokens, 0);
+    const int64_t nq = std::max<int32_t>(num_queues, 1);
+    // prefill row blocks: at most one per kPrefillRows rows plus one per sequence
+    const int64_t blocks = toks / kPrefillRows + seqs;
+    const int64_t prefill_units = blocks * kPrefillMaxPieces;
+    const int64_t units = nq + seqs + prefill_units;
+    const int64_t merges = seqs + blocks;
+    const int64_t prows = nq + seqs + toks * kPrefillMaxPieces;
+    const size_t image = align_up(static_cast<size_t>(units) * sizeof(Unit)) +
+                         align_up(static_cast<size_t>(nq + 1) * sizeof(int32_t)) +
+                         align_up(static_cast<size_t>(merges) * sizeof(Merge));
+    const size_t hd = static_cast<size_t>(std::max(num_q_heads, 1)) * static_cast<size_t>(std::max(head_dim, 1));
+    const size_t po = align_up(static_cast<size_t>(prows) * hd * sizeof(float));
+    const size_t pl = align_up(static_cast<size_t>(prows) * static_cast<size_t>(std::max(num_q_heads, 1)) * sizeof(float));
+    if (workspace_bytes) *workspace_bytes = image + po + pl;
+    if (host_bytes) *host_bytes = image;
+}
+
+}  // namespace pkv

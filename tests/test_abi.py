@@ -1,0 +1,230 @@
+"""CPU tests of the C-ABI library: it loads, exports what include/pkv.h declares,
+its host planner reproduces the oracle's plan exactly, and its argument checks
+return the documented status before anything is launched.
+
+The argument-check tests pass dummy device addresses: they are skipped when a
+GPU is present so that a checking bug can never launch a kernel on them.
+"""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_write_amd as pkv
+from paged_kv_attention_write_amd import _abi
+from oracle.plan import split_kv_plan
+from conftest import gpu_available
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+cpu_only = pytest.mark.skipif(gpu_available(), reason="dummy-pointer checks run on the CPU tier only")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = pkv.lib()
+    declared = _header_functions()
+    assert set(declared) == set(_abi.EXPORTS), declared
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.pkv_abi_version() == 1
+
+
+def test_strerror_covers_all_codes():
+    for code in range(0, -8, -1):
+        msg = pkv.strerror(code)
+        assert msg and msg != "unknown status"
+    assert pkv.strerror(-99) == "unknown status"
+
+
+def _queues_from_image(p, image):
+    units, qoff, _ = pkv.decode_plan_image(p, image)
+    out = []
+    for q in range(p.num_queues):
+        out.append([(int(u[0]), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]])
+    return out
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("nq", [1, 5, 64, 512])
+def test_native_plan_equals_oracle_plan(seed, nq):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, 5000, size=int(rng.integers(1, 100)))
+    p, image = pkv.plan_host(lens, None, 32, 8, 128, nq)
+    assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq)
+
+
+@pytest.mark.parametrize("config", ["tiny", "decode", "long", "fp8prefix"])
+def test_native_plan_equals_oracle_plan_on_workloads(config):
+    import workloads
+
+    lens = workloads.decode_lengths(config)
+    for nq in (256, 512):
+        p, image = pkv.plan_host(lens, None, 32, 8, 128, nq)
+        assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq)
+
+
+def test_plan_partials_and_merges_are_consistent():
+    rng = np.random.default_rng(3)
+    lens = rng.integers(1, 3000, size=50)
+    p, image = pkv.plan_host(lens, None, 32, 8, 128, 37)
+    units, qoff, merges = pkv.decode_plan_image(p, image)
+    assert qoff[0] == 0 and qoff[-1] == p.num_units and np.all(np.diff(qoff) >= 0)
+    prows = units[units[:, 6] >= 0, 6]
+    assert len(set(prows.tolist())) == len(prows) == p.num_partial_rows
+    for row0, nrows, prow0, parts in merges:
+        assert nrows == 1
+        mine = units[(units[:, 0] == row0) & (units[:, 6] >= 0)]
+        mine = mine[np.argsort(mine[:, 1])]
+        assert len(mine) == parts >= 2
+        assert list(mine[:, 6]) == [prow0 + c for c in range(parts)]
+    split = {int(m[0]) for m in merges}
+    whole = units[units[:, 6] < 0]
+    assert not split & set(whole[:, 0].tolist())
+    assert p.workspace_bytes >= p.off_partial_lse + 4 * 32 * p.num_partial_rows
+
+
+def _mixed_case():
+    rng = np.random.default_rng(11)
+    dec = rng.integers(256, 2049, size=20)
+    lens = np.concatenate([dec, [2560, 700, 130]])
+    ql = np.concatenate([np.ones(20, int), [512, 700, 65]])
+    return lens.astype(np.int32), ql.astype(np.int32)
+
+
+def test_mixed_plan_covers_every_visible_pair_once():
+    lens, ql = _mixed_case()
+    p, image = pkv.plan_host(lens, ql, 32, 8, 128, 96)
+    units, qoff, merges = pkv.decode_plan_image(p, image)
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    assert p.num_tokens == cu[-1] and p.max_q_len == 700
+    for s in range(len(lens)):
+        n, L = int(lens[s]), int(ql[s])
+        cover = np.zeros((L, n), np.int32)
+        for u in units[units[:, 0] == s]:
+            seq, kb, ke, row0, nrows, pos0, prow, kind = (int(x) for x in u)
+            assert kind == (1 if L > 1 else 0)
+            r = row0 - cu[s]
+            assert pos0 == n - L + r
+            for i in range(nrows):
+                pos = pos0 + i
+                lo, hi = kb, min(ke, pos + 1)
+                if hi > lo:
+                    cover[r + i, lo:hi] += 1
+        visible = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]
+        assert np.array_equal(cover, visible.astype(np.int32)), s
+    # every merged block lists its pieces at prow0 + c * nrows
+    for row0, nrows, prow0, parts in merges:
+        us = units[(units[:, 3] == row0) & (units[:, 6] >= 0)]
+        assert sorted(us[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
+
+
+def test_workspace_bound_covers_plans():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        B = int(rng.integers(1, 80))
+        lens = rng.integers(1, 9000, size=B).astype(np.int32)
+        ql = np.where(rng.random(B) < 0.2, rng.integers(1, 300, size=B), 1).astype(np.int32)
+        ql = np.minimum(ql, lens)
+        nq = int(rng.integers(1, 600))
+        p, _ = pkv.plan_host(lens, ql, 16, 4, 128, nq)
+        ws, host = _sizes(B, int(ql.sum()), 16, 128, nq)
+        assert ws >= p.workspace_bytes and host >= p.image_bytes
+
+
+def _sizes(max_seqs, max_tokens, hq, d, nq):
+    import ctypes
+
+    ws, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = pkv.lib().paged_attn_workspace_size(max_seqs, max_tokens, hq, d, nq, ctypes.byref(ws), ctypes.byref(host))
+    assert st == 0
+    return ws.value, host.value
+
+
+def test_plan_host_rejects_bad_lengths_and_shapes():
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_host([5, 3], [1, 4], 8, 2, 64, 4)          # q_len > context_len
+    assert e.value.status == _abi.PKV_ERR_SHAPE
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_host([5, -1], None, 8, 2, 64, 4)
+    assert e.value.status == _abi.PKV_ERR_SHAPE
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_host([5], None, 6, 4, 64, 4)               # Hq % H_kv != 0
+    assert e.value.status == _abi.PKV_ERR_SHAPE
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.plan_host([5], None, 8, 2, 64, 0)               # no queues
+    assert e.value.status == _abi.PKV_ERR_SHAPE
+    p, image = pkv.plan_host([], None, 8, 2, 64, 3)          # empty batch is fine
+    assert p.num_units == 0 and p.num_tokens == 0
+
+
+# ---------------------------------------------------------------------------
+# argument checks that return before any launch (dummy addresses, CPU only)
+# ---------------------------------------------------------------------------
+
+A = 1 << 20  # a 1 MiB-aligned dummy address; never dereferenced by these calls
+
+
+def _write(**kw):
+    args = dict(k_new=A, v_new=A, new_dtype=1, stride=1024, slots=A, T=4, kc=A, vc=A, cache_dtype=1, nb=8, bs=16,
+                hkv=8, d=128, ks=1.0, vs=1.0, stream=None)
+    args.update(kw)
+    return pkv.lib().paged_kv_write(*args.values())
+
+
+@cpu_only
+def test_write_argument_checks():
+    assert _write(new_dtype=7) == _abi.PKV_ERR_DTYPE
+    assert _write(new_dtype=2) == _abi.PKV_ERR_DTYPE          # fp8 is a cache dtype only
+    assert _write(new_dtype=1, cache_dtype=0) == _abi.PKV_ERR_UNSUPPORTED  # bf16 -> f32 not offered
+    assert _write(d=12) == _abi.PKV_ERR_SHAPE
+    assert _write(stride=1000) == _abi.PKV_ERR_SHAPE           # < H_kv * D
+    assert _write(bs=0) == _abi.PKV_ERR_SHAPE
+    assert _write(cache_dtype=2, ks=0.0) == _abi.PKV_ERR_SHAPE
+    assert _write(cache_dtype=2, vs=float("nan")) == _abi.PKV_ERR_SHAPE
+    assert _write(k_new=None) == _abi.PKV_ERR_NULL
+    assert _write(slots=None) == _abi.PKV_ERR_NULL
+    assert _write(k_new=A + 4) == _abi.PKV_ERR_SHAPE           # misaligned
+    assert _write(T=0, k_new=None, slots=None) == _abi.PKV_OK   # nothing to do
+
+
+def _decode(the_plan, **kw):
+    import ctypes
+
+    args = dict(out=A, q=A, q_dtype=1, q_stride=4096, kc=A, vc=A, kv_dtype=1, tables=A, max_blocks=64,
+                ctx=A, B=4, hq=32, hkv=8, d=128, nb=1000, bs=16, scale=0.088, ks=1.0, vs=1.0,
+                plan=ctypes.byref(the_plan), ws=A, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return pkv.lib().paged_attn_decode(*args.values())
+
+
+@cpu_only
+def test_decode_argument_checks():
+    import ctypes
+
+    p, _ = pkv.plan_host([100, 200, 300, 400], None, 32, 8, 128, 16)
+    assert _decode(p, q_dtype=2) == _abi.PKV_ERR_DTYPE
+    assert _decode(p, kv_dtype=9) == _abi.PKV_ERR_DTYPE
+    assert _decode(p, d=96) == _abi.PKV_ERR_UNSUPPORTED
+    assert _decode(p, hkv=3) == _abi.PKV_ERR_SHAPE
+    assert _decode(p, hq=48, hkv=3) == _abi.PKV_ERR_UNSUPPORTED   # group 16
+    assert _decode(p, q_dtype=0) == _abi.PKV_ERR_UNSUPPORTED      # f32 q with bf16 cache
+    assert _decode(p, kv_dtype=2, ks=-1.0) == _abi.PKV_ERR_SHAPE
+    assert _decode(p, q_stride=100) == _abi.PKV_ERR_SHAPE
+    assert _decode(p, plan=None) == _abi.PKV_ERR_NULL
+    assert _decode(p, B=5) == _abi.PKV_ERR_PLAN                   # plan made for 4 sequences
+    assert _decode(p, hq=16) == _abi.PKV_ERR_PLAN
+    assert _decode(p, ws_bytes=16) == _abi.PKV_ERR_WORKSPACE
+    assert _decode(p, out=None) == _abi.PKV_ERR_NULL
+    assert _decode(p, q=A + 2) == _abi.PKV_ERR_SHAPE
+    stale = _abi.PkvPlan()
+    assert _decode(p, plan=ctypes.byref(stale)) == _abi.PKV_ERR_PLAN
+    pm, _ = pkv.plan_host([100, 200, 300, 400], [1, 1, 1, 50], 32, 8, 128, 16)
+    assert _decode(pm, B=4) == _abi.PKV_ERR_PLAN                  # a mixed plan is not a decode plan

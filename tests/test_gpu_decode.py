@@ -1,0 +1,201 @@
+"""GPU parity of paged_attn_decode (with its write) against the fp64 oracle.
+
+Tolerances (max-abs error against the oracle): 1e-4 for fp32 K/V, 2e-2 for
+bf16 K/V, 6e-2 for an fp8 cache.  Each case prints its name before it runs.
+Unused pool slots and table entries past a sequence are poisoned (NaN / -1),
+so a stray read shows up as NaN.
+"""
+
+import numpy as np
+import pytest
+
+import workloads
+from gpu_helpers import (TOL, DeviceCase, as_f64, log, max_err, oracle_attention, oracle_caches, to_dev,
+                         to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, gpu, num_queues=0, seqs=None):
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    plan = dc.plan(num_queues)
+    out = as_f64(dc.decode(plan))
+    kr, vr = oracle_caches(case, inplace=True)  # the device holds its own copy
+    assert np.array_equal(to_host(dc.kc).view(np.uint8), kr.view(np.uint8)), "cache after write differs"
+    ref, _ = oracle_attention(case, kr, vr, seqs=seqs)
+    rows = np.arange(case.num_tokens) if seqs is None else np.asarray(seqs)
+    return out[rows], ref[rows], plan, dc
+
+
+@pytest.mark.parametrize("num_queues", [0, 1, 3, 4, 12, 1000])
+def test_tiny_fp32(gpu, num_queues):
+    log(f"tiny fp32 queues={num_queues}")
+    case = workloads.make_case("tiny")
+    got, ref, plan, _ = _run(case, gpu, num_queues)
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e} merges={plan.desc.num_merges}")
+    assert np.all(np.isfinite(got)) and err <= TOL["f32"]
+
+
+def test_decode_workload_full_size(gpu):
+    """64 x U[512, 4096] at 32/8/128 bf16, default queues (the benchmark's launch)."""
+    log("decode full size")
+    case = workloads.make_case("decode")
+    got, ref, plan, _ = _run(case, gpu)
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e} units={plan.desc.num_units} merges={plan.desc.num_merges}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("bs", [1, 3, 7, 16, 32])
+@pytest.mark.parametrize("num_queues", [1, 9, 0])
+def test_block_sizes(gpu, bs, num_queues):
+    log(f"block size {bs} queues={num_queues}")
+    lens = [1, 17, 100, 250, 513, 64]
+    case = workloads.build_case(f"bs{bs}", 40 + bs, lens, [1] * len(lens), num_q_heads=16, num_kv_heads=4,
+                                head_dim=128, block_size=bs)
+    got, ref, _, _ = _run(case, gpu, num_queues)
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (8, 1, 128), (16, 8, 64), (32, 4, 128), (64, 8, 128),
+                                      (4, 2, 64)])
+def test_head_shapes(gpu, hq, hkv, d):
+    log(f"heads {hq}/{hkv} d={d}")
+    lens = [5, 300, 77, 1024]
+    case = workloads.build_case("heads", 50, lens, [1] * 4, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                block_size=16)
+    got, ref, _, _ = _run(case, gpu, 7)
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
+
+
+def test_permutation_and_sharing_are_bit_identical(gpu):
+    """Same logical K/V under another table permutation, and with a shared prefix
+    against private copies: byte-identical outputs (arithmetic follows logical
+    positions only; the plan follows lengths only)."""
+    import paged_kv_attention_write_amd as pkv
+    from paging import page_out
+
+    rng = np.random.default_rng(8)
+    hkv, d = 4, 128
+    prefix = workloads.to_storage(rng.standard_normal((96, hkv, d)).astype(np.float32), "bf16")
+    prefv = workloads.to_storage(rng.standard_normal((96, hkv, d)).astype(np.float32), "bf16")
+    K, V = [], []
+    for n in (40, 400, 17, 96):
+        K.append(np.concatenate([prefix, workloads.to_storage(rng.standard_normal((n, hkv, d)).astype(np.float32), "bf16")]))
+        V.append(np.concatenate([prefv, workloads.to_storage(rng.standard_normal((n, hkv, d)).astype(np.float32), "bf16")]))
+    lens = np.array([k.shape[0] for k in K], np.int32)
+    q = workloads.to_storage(rng.standard_normal((4, 16, d)).astype(np.float32), "bf16")
+    qd = to_dev(q, gpu)
+    plan = pkv.Plan(lens, num_q_heads=16, num_kv_heads=hkv, head_dim=d, device=gpu, num_queues=11)
+    outs = []
+    for layout in (dict(perm_seed=None), dict(perm_seed=3, extra_blocks=9), dict(perm_seed=5, shared_prefix_blocks=6)):
+        kp, vp, tab = page_out(K, V, 16, **layout)
+        o = to_dev(np.zeros_like(q), gpu)
+        pkv.paged_attn_decode(o, qd, to_dev(kp, gpu), to_dev(vp, gpu), to_dev(tab, gpu), to_dev(lens, gpu),
+                              0.08838834764831845, plan)
+        outs.append(to_host(o))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_neighbour_independence(gpu):
+    """A sequence batched with others gets its oracle answer whatever the others are."""
+    base = [300, 1000, 20]
+    for extra in ([], [4000, 4000], [1] * 30):
+        lens = base + extra
+        case = workloads.build_case("nb", 60, lens, [1] * len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                    block_size=16)
+        got, ref, _, _ = _run(case, gpu, 0)
+        assert max_err(got, ref) <= TOL["bf16"]
+
+
+def test_invalid_block_id_gives_nan_rows_only_for_that_sequence(gpu):
+    """A table entry outside the pool is never dereferenced; its sequence's rows
+    come out NaN and the other sequences are unaffected."""
+    import paged_kv_attention_write_amd as pkv
+
+    case = workloads.build_case("badid", 61, [50, 200, 33], [1, 1, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                block_size=16)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    tables = case.block_tables.copy()
+    tables[1, 5] = case.num_blocks + 1000
+    dc.tables = to_dev(tables, gpu)
+    out = as_f64(dc.decode(dc.plan(5)))
+    assert np.all(np.isnan(out[1]))
+    assert max_err(out[[0, 2]], ref[[0, 2]]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("layout", ["page1", "page16", "contig"])
+def test_long_context_layouts_sampled(gpu, layout):
+    """16 x 32768 at page 1 (shuffled), page 16 (shuffled) or a contiguous slab;
+    3 sampled sequences against the oracle."""
+    log(f"long {layout}")
+    case = workloads.make_case("long", layout)
+    got, ref, plan, _ = _run(case, gpu, seqs=[0, 7, 15])
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e} units={plan.desc.num_units}")
+    assert np.all(np.isfinite(got)) and err <= TOL["bf16"]
+
+
+def test_fp8_prefix_shared_full_size(gpu):
+    """128 sequences sharing 256 blocks, fp8 cache filled by the quantising write."""
+    log("fp8 prefix")
+    case = workloads.make_case("fp8prefix")
+    got, ref, plan, _ = _run(case, gpu, seqs=list(range(0, 128, 9)))
+    err = max_err(got, ref)
+    log(f"  max abs err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_small(gpu, d):
+    case = workloads.build_case("fp8s", 62, [3, 70, 500, 16], [1] * 4, num_q_heads=16, num_kv_heads=4, head_dim=d,
+                                block_size=16, kv_dtype="fp8")
+    got, ref, _, _ = _run(case, gpu, 6)
+    assert np.all(np.isfinite(got)) and max_err(got, ref) <= TOL["fp8"]
+
+
+def test_q_token_stride(gpu):
+    """q taken from a fused projection output with a token stride."""
+    import torch
+
+    import paged_kv_attention_write_amd as pkv
+
+    case = workloads.build_case("qs", 63, [40, 300], [1, 1], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                block_size=16)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    wide = torch.zeros((2, 12 * 128), dtype=torch.bfloat16, device=gpu)
+    wide[:, :8 * 128] = dc.q.view(2, -1)
+    qv = wide[:, :8 * 128].view(2, 8, 128)
+    assert not qv.is_contiguous()
+    out = torch.empty((2, 8, 128), dtype=torch.bfloat16, device=gpu)
+    pkv.paged_attn_decode(out, qv, dc.kc, dc.vc, dc.tables, dc.ctx, case.scale, dc.plan(3))
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    assert max_err(as_f64(out), ref) <= TOL["bf16"]
+
+
+def test_plan_reused_across_layers(gpu):
+    """One plan, several layers with their own pools and queries (the pages' step)."""
+    lens = [100, 900, 2000]
+    plan = None
+    for layer in range(3):
+        case = workloads.build_case("layer", 70 + layer, lens, [1, 1, 1], num_q_heads=8, num_kv_heads=2,
+                                    head_dim=128, block_size=16)
+        dc = DeviceCase(case, gpu)
+        dc.write()
+        if plan is None:
+            plan = dc.plan(4)
+        got = as_f64(dc.decode(plan))
+        kr, vr = oracle_caches(case)
+        ref, _ = oracle_attention(case, kr, vr)
+        assert max_err(got, ref) <= TOL["bf16"]

@@ -62,8 +62,20 @@ def to_storage(x_f32: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         import torch
 
-        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     raise ValueError(f"inputs are drawn as f32 or bf16, not {dtype}")
+
+
+def draw(config_id: int, stream: int, shape, dtype: str, chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, 1) fp32 draws of one random stream, rounded to ``dtype`` chunk by
+    chunk straight into the output array (no full-size fp32 temporary)."""
+    rng = rng_for(config_id, stream)
+    out = np.empty(shape, dtype=STORAGE_NP[dtype])
+    flat = out.reshape(-1)
+    for i in range(0, flat.size, chunk):
+        n = min(chunk, flat.size - i)
+        flat[i:i + n] = to_storage(rng.standard_normal(n, dtype=np.float32), dtype)
+    return out
 
 
 @dataclasses.dataclass
@@ -187,11 +199,11 @@ def build_case(
 
     shape = (nblocks, bs, hkv, d)
     src_dtype = new_dtype if kv_dtype == "fp8" else kv_dtype
-    k_pool = to_storage(rng_for(config_id, 2).standard_normal(shape, dtype=np.float32), src_dtype)
-    v_pool = to_storage(rng_for(config_id, 3).standard_normal(shape, dtype=np.float32), src_dtype)
-    q = to_storage(rng_for(config_id, 4).standard_normal((T, int(num_q_heads), d), dtype=np.float32), q_dtype)
-    k_new = to_storage(rng_for(config_id, 5).standard_normal((T, hkv, d), dtype=np.float32), new_dtype)
-    v_new = to_storage(rng_for(config_id, 6).standard_normal((T, hkv, d), dtype=np.float32), new_dtype)
+    k_pool = draw(config_id, 2, shape, src_dtype)
+    v_pool = draw(config_id, 3, shape, src_dtype)
+    q = draw(config_id, 4, (T, int(num_q_heads), d), q_dtype)
+    k_new = draw(config_id, 5, (T, hkv, d), new_dtype)
+    v_new = draw(config_id, 6, (T, hkv, d), new_dtype)
 
     fill_slots = k_fill = v_fill = None
     k_scale = v_scale = 1.0
