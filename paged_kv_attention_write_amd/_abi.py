@@ -156,10 +156,10 @@ def _stream(stream, device) -> Optional[int]:
 
 
 def _inner_contiguous(t, inner: int, name: str) -> None:
-    if t.dim() < 2 or not t[0].is_contiguous() or t.stride(-1) != 1:
+    if t.dim() < 2 or t.shape[1:].numel() != inner:
+        raise ValueError(f"{name}: expected [T, ...] with {inner} elements per token")
+    if t.shape[0] and (not t[0].is_contiguous() or t.stride(-1) != 1):
         raise ValueError(f"{name}: the per-token [heads, dim] block must be contiguous")
-    if t.numel() and t.shape[1:].numel() != inner:
-        raise ValueError(f"{name}: expected {inner} elements per token")
 
 
 def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,

@@ -29,6 +29,11 @@ struct AttnArgs {
     float* partial_lse;           // [rows][hq], log2 units
 };
 
+__device__ __forceinline__ Unit load_unit(const_ptr<Unit> units, int i) {
+    const const_ptr<int32_t> w = reinterpret_cast<const_ptr<int32_t>>(units + i);
+    return Unit{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+}
+
 // Store EPL fp32 values as the output dtype (bf16: round to nearest even).
 template <int QDT, int EPL>
 __device__ __forceinline__ void store_out(char* dst, const float (&o)[EPL]) {
