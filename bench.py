@@ -142,6 +142,58 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
                       f"{reps} repetition(s), fp64 NumPy oracle", "out": out}
 
 
+COPY_BYTES = 1 << 30
+
+# Sources that define the kernels of one paged_attn_decode call (decode and
+# merge kernels, the plan they walk).  A traffic record taken from the byte
+# counters is reported only while these sources are unchanged.
+DECODE_SOURCES = ["pkv_decode.hip", "pkv_device.h", "pkv_attention.h", "pkv_internal.h", "pkv_plan.cpp"]
+
+
+def decode_source_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_write_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config):
+    """HBM bytes per call from a committed counter summary (profiles/*.md,
+    a line 'traffic-record: {json}'), or None if there is none for this
+    config or the kernels changed since it was taken."""
+    d = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(d):
+        return None
+    digest = decode_source_digest()
+    for name in sorted(os.listdir(d)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(d, name)) as fh:
+            for line in fh:
+                if line.startswith("traffic-record:"):
+                    rec = json.loads(line.split(":", 1)[1])
+                    if rec.get("config") == config and rec.get("source_sha256") == digest:
+                        return rec
+    return None
+
+
+def copy_calibration(torch):
+    """A plain 1 GiB device-to-device copy, three times: under a counter run
+    its FETCH_SIZE / WRITE_SIZE per dispatch against 1 GiB read / written
+    gives the factor that turns those counters into bytes."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "dispatches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +203,8 @@ def main():
     ap.add_argument("--config", default="decode", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); sharding across GPUs is not built",
@@ -158,6 +212,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import paged_kv_attention_write_amd as pkv
     import workloads
@@ -263,6 +321,10 @@ def main():
         "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
                  "merges": int(plan.desc.num_merges), "target_tiles": int(plan.desc.target_tiles)},
     }
+    rec = recorded_traffic(args.config)
+    if rec is not None:
+        result["roofline"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])
+        result["roofline"]["traffic_source"] = rec["profile"]
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         cb = cpu_baseline(torch, st, layers[0], kv_dtype, scales[0], args.cpu_budget)

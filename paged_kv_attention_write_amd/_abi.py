@@ -222,9 +222,12 @@ def default_queues() -> int:
 class Plan:
     """A split-KV plan in a device workspace, reusable by every layer of a step.
 
-    Holds the plan descriptor, a pinned host staging buffer for the upload and
-    the device workspace (both allocated through torch).  ``update`` re-plans
-    for new lengths into the same buffers when they are large enough.
+    Holds the plan descriptor, two pinned host staging buffers used in turn
+    for the upload (so a new plan never waits for the previous upload) and
+    the device workspace (all allocated through torch).  ``update`` re-plans
+    for new lengths into the same buffers when they are large enough.  The
+    upload is ordered on the stream like any kernel, so a re-plan issued
+    after the previous step's attention calls on the same stream is safe.
     """
 
     def __init__(self, context_lens, q_lens=None, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -234,9 +237,10 @@ class Plan:
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         with torch.cuda.device(self.device):
             self.num_queues = int(num_queues) if num_queues and num_queues > 0 else default_queues()
-        self.staging = None
+        self._staging = [None, None]
+        self._uploaded = [None, None]
+        self._turn = 0
         self.workspace = None
-        self._uploaded = None
         self.desc = PkvPlan()
         self.update(context_lens, q_lens, stream=stream)
 
@@ -245,25 +249,37 @@ class Plan:
         ctx = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
         ql = None if q_lens is None else np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
         ql_ptr = None if ql is None else ql.ctypes.data
-        probe = PkvPlan()
-        _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
-                                          self.num_kv_heads, self.head_dim, self.num_queues, None, 0,
-                                          ctypes.byref(probe)), "paged_attn_plan_host")
-        if self._uploaded is not None:
-            self._uploaded.synchronize()  # the staging buffer's last upload has run
-        if self.staging is None or self.staging.numel() < probe.image_bytes:
-            self.staging = torch.empty(max(int(probe.image_bytes), 256), dtype=torch.uint8, pin_memory=True)
-        if self.workspace is None or self.workspace.numel() < probe.workspace_bytes:
-            self.workspace = torch.empty(max(int(probe.workspace_bytes), 256), dtype=torch.uint8, device=self.device)
+        i = self._turn
+        self._turn ^= 1
+        if self._uploaded[i] is not None:
+            self._uploaded[i].synchronize()  # this staging buffer's last upload (two updates ago) has run
         with torch.cuda.device(self.device):
-            st = lib().paged_attn_plan(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads, self.num_kv_heads,
-                                       self.head_dim, self.num_queues, self.staging.data_ptr(),
-                                       self.staging.numel(), self.workspace.data_ptr(), self.workspace.numel(),
-                                       ctypes.byref(self.desc), _stream(stream, self.device))
+            st_ptr = _stream(stream, self.device)
+            for attempt in range(2):
+                staging, ws = self._staging[i], self.workspace
+                st = lib().paged_attn_plan(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads, self.num_kv_heads,
+                                           self.head_dim, self.num_queues,
+                                           staging.data_ptr() if staging is not None else None,
+                                           staging.numel() if staging is not None else 0,
+                                           ws.data_ptr() if ws is not None else None,
+                                           ws.numel() if ws is not None else 0, ctypes.byref(self.desc), st_ptr)
+                if st in (PKV_ERR_WORKSPACE, PKV_ERR_NULL) and attempt == 0:
+                    probe = PkvPlan()
+                    _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                                      self.num_kv_heads, self.head_dim, self.num_queues, None, 0,
+                                                      ctypes.byref(probe)), "paged_attn_plan_host")
+                    if staging is None or staging.numel() < probe.image_bytes:
+                        self._staging[i] = torch.empty(max(int(probe.image_bytes), 256), dtype=torch.uint8,
+                                                       pin_memory=True)
+                    if ws is None or ws.numel() < probe.workspace_bytes:
+                        self.workspace = torch.empty(max(int(probe.workspace_bytes), 256), dtype=torch.uint8,
+                                                     device=self.device)
+                    continue
+                break
             _check(st, "paged_attn_plan")
             ev = torch.cuda.Event()
             ev.record(torch.cuda.current_stream(self.device) if stream is None else stream)
-            self._uploaded = ev
+            self._uploaded[i] = ev
         self.context_lens = ctx
         self.q_lens = ql
         return self

@@ -12,20 +12,23 @@ namespace pkv {
 // Work is counted in tiles of this many keys; piece boundaries inside a
 // sequence fall on tile boundaries.
 constexpr int kTileTokens = 16;
-// Rows of a query chunk handled by one prefill unit.
-constexpr int kPrefillRows = 64;
-// Key pieces of a prefill row block: at least this long, at most this many.
-constexpr int kPrefillPieceMin = 512;
+// A prefill unit covers this many (row, q head) pairs of one kv head: the
+// rows of a chunk are taken in blocks of kPrefillQRows / G rows (G = q heads
+// per kv head), each block times each kv head times each key piece.
+constexpr int kPrefillQRows = 128;
+// Key pieces of one prefill row block: at most this many.  A piece is cut so
+// that its cost stays within one queue's share of the step.
 constexpr int kPrefillMaxPieces = 8;
 // Cost of a prefill unit in decode tiles: one tile of decode work (16 keys of
-// 8 kv heads x 128 dims in bf16, 64 KiB) takes as long as this many flops of
-// matrix-core work at the rates the kernels reach (HBM ~6 TB/s against
-// ~1.2 PFLOP/s of bf16 MFMA).
-constexpr double kFlopsPerTile = 13.0e6;
+// 8 kv heads x 128 dims in bf16, 64 KiB) takes a queue about as long as this
+// many flops of matrix-core work.
+constexpr int64_t kFlopsPerTile = 13000000;
 
 // Alignment of the sections of the workspace.
 constexpr size_t kAlign = 256;
 
+// kind == kUnitDecode: a decode unit (one row, every kv head).  kind >= 1: a
+// prefill unit of kv head kind - 1.
 enum UnitKind : int32_t { kUnitDecode = 0, kUnitPrefill = 1 };
 
 // One piece of work: query rows [row0, row0 + nrows) of sequence `seq` (rows

@@ -9,9 +9,11 @@
 // share, so queues end within one tile of each other and a request is cut
 // only where a queue fills up (at most queues + requests pieces in all).
 //
-// Query chunks (more than one new row) are split into blocks of rows and key
-// pieces first; each (row block, key piece) pair is one whole unit whose cost
-// is its matrix-core work expressed in tiles, and these units are placed
+// Query chunks (more than one new row) are split into blocks of rows, one
+// unit per (row block, kv head, key piece); a unit's cost is its matrix-core
+// work expressed in tiles, the key range of a row block is cut so that no
+// piece costs more than the share, and these units are placed before the
+// decode requests, largest first.
 // before the decode requests, largest first.
 #include <algorithm>
 #include <cstring>
@@ -76,8 +78,36 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     row0[num_seqs] = static_cast<int32_t>(rows);
 
     const int64_t hd = static_cast<int64_t>(num_q_heads) * head_dim;
+    const int32_t group = num_q_heads / num_kv_heads;
+    const int32_t block_rows = std::max(1, kPrefillQRows / group);
 
-    // Prefill units: row blocks x key pieces of every chunk.
+    // visible (row, key) pairs of rows [r0, r1) of a chunk of L rows over n
+    // keys, against keys [kb, ke)
+    auto pairs_of = [](int32_t n, int32_t L, int32_t r0, int32_t r1, int64_t kb, int64_t ke) {
+        int64_t pairs = 0;
+        for (int32_t r = r0; r < r1; ++r) {
+            const int64_t last = static_cast<int64_t>(n) - L + r;  // position of row r
+            pairs += std::max<int64_t>(0, std::min<int64_t>(ke - 1, last) - kb + 1);
+        }
+        return pairs;
+    };
+    // flops of one kv head: 2 (q.k) + 2 (p.v) per pair, q head and dimension
+    const int64_t flops_per_pair = 4LL * group * head_dim;
+
+    // Total work and the share per queue.
+    int64_t decode_tiles = 0;
+    int64_t prefill_flops = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = ctx[s];
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (L == 1) decode_tiles += ceil_div(n, kTileTokens);
+        if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
+    }
+    // first share: cuts the key ranges of the prefill row blocks
+    const int64_t total0 = decode_tiles + ceil_div(prefill_flops, kFlopsPerTile);
+    const int64_t target0 = total0 > 0 ? ceil_div(total0, num_queues) : 0;
+
+    // Prefill units: row blocks x kv heads x key pieces of every chunk.
     std::vector<PrefillPiece> prefill;
     std::vector<Merge> merges;
     int64_t partial_rows = 0;
@@ -85,43 +115,41 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         const int32_t n = ctx[s];
         const int32_t L = q_lens ? q_lens[s] : 1;
         if (L <= 1) continue;
-        for (int32_t r0 = 0; r0 < L; r0 += kPrefillRows) {
-            const int32_t r1 = std::min(L, r0 + kPrefillRows);
+        for (int32_t r0 = 0; r0 < L; r0 += block_rows) {
+            const int32_t r1 = std::min(L, r0 + block_rows);
             const int32_t nr = r1 - r0;
             const int32_t extent = n - L + r1;  // keys the last row of the block sees
-            int64_t piece = std::max<int64_t>(kPrefillPieceMin, ceil_div(extent, kPrefillMaxPieces));
-            piece = ceil_div(piece, kTileTokens) * kTileTokens;
-            const int32_t parts = static_cast<int32_t>(ceil_div(extent, piece));
+            // tiles of the longest piece whose full-width cost fits the share
+            const int64_t per_tile = static_cast<int64_t>(nr) * flops_per_pair * kTileTokens;
+            const int64_t fit = std::max<int64_t>(1, target0 * kFlopsPerTile / per_tile);
+            const int64_t want = ceil_div(ceil_div(extent, kTileTokens), fit);
+            const int64_t ask = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, want));
+            const int64_t piece = ceil_div(ceil_div(extent, ask), kTileTokens) * kTileTokens;
+            const int32_t parts = static_cast<int32_t>(ceil_div(extent, piece));  // no empty piece
             const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
             if (parts > 1) {
                 merges.push_back(Merge{row0[s] + r0, nr, prow0, parts});
                 partial_rows += static_cast<int64_t>(parts) * nr;
             }
             for (int32_t c = 0; c < parts; ++c) {
-                const int32_t kb = static_cast<int32_t>(c * piece);
-                const int32_t ke = static_cast<int32_t>(std::min<int64_t>(extent, kb + piece));
-                // visible (row, key) pairs of the unit
-                int64_t pairs = 0;
-                for (int32_t r = r0; r < r1; ++r) {
-                    const int64_t last = static_cast<int64_t>(n) - L + r;  // position of row r
-                    pairs += std::max<int64_t>(0, std::min<int64_t>(ke - 1, last) - kb + 1);
+                const int64_t kb = c * piece;
+                const int64_t ke = std::min<int64_t>(extent, kb + piece);
+                const int64_t flops = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
+                const int64_t cost = std::max<int64_t>(1, (flops + kFlopsPerTile / 2) / kFlopsPerTile);
+                for (int32_t h = 0; h < num_kv_heads; ++h) {
+                    const Unit u{s, static_cast<int32_t>(kb), static_cast<int32_t>(ke), row0[s] + r0, nr,
+                                 n - L + r0, parts > 1 ? prow0 + c * nr : -1, kUnitPrefill + h};
+                    prefill.push_back(PrefillPiece{u, cost, static_cast<int32_t>(prefill.size())});
                 }
-                const double flops = 4.0 * static_cast<double>(pairs) * static_cast<double>(hd);
-                const int64_t cost = std::max<int64_t>(1, static_cast<int64_t>(flops / kFlopsPerTile + 0.5));
-                Unit u{s, kb, ke, row0[s] + r0, nr, n - L + r0, parts > 1 ? prow0 + c * nr : -1,
-                       kUnitPrefill};
-                prefill.push_back(PrefillPiece{u, cost, static_cast<int32_t>(prefill.size())});
             }
         }
     }
 
-    // Total work and the share per queue.
-    int64_t total = 0;
+    // The share of the placement: the units' own (rounded) costs plus the
+    // decode tiles, so that the queues together hold exactly the total and a
+    // queue below the share exists while any work is left.
+    int64_t total = decode_tiles;
     for (const auto& p : prefill) total += p.cost;
-    for (int32_t s = 0; s < num_seqs; ++s) {
-        const int32_t L = q_lens ? q_lens[s] : 1;
-        if (L == 1) total += ceil_div(ctx[s], kTileTokens);
-    }
     const int64_t target = total > 0 ? ceil_div(total, num_queues) : 0;
 
     std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
@@ -150,7 +178,9 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         placed.clear();
         while (remaining > 0) {
             auto [load, q] = heap.pop();
-            const int64_t take = std::min(remaining, target - load);
+            // never reached while a queue is below the share; kept so that a
+            // full lightest queue takes the rest instead of looping
+            const int64_t take = target > load ? std::min(remaining, target - load) : remaining;
             const int32_t kb = static_cast<int32_t>(first * kTileTokens);
             const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, (first + take) * kTileTokens));
             queues[q].push_back(Unit{s, kb, ke, row0[s], 1, n - 1, -1, kUnitDecode});
@@ -226,9 +256,13 @@ void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int3
     const int64_t seqs = std::max<int32_t>(max_seqs, 0);
     const int64_t toks = std::max<int32_t>(max_tokens, 0);
     const int64_t nq = std::max<int32_t>(num_queues, 1);
-    // prefill row blocks: at most one per kPrefillRows rows plus one per sequence
-    const int64_t blocks = toks / kPrefillRows + seqs;
-    const int64_t prefill_units = blocks * kPrefillMaxPieces;
+    // prefill row blocks: blocks of kPrefillQRows / G >= kPrefillQRows /
+    // num_q_heads rows, at most one partial block per sequence; a unit per kv
+    // head (<= num_q_heads) and piece
+    const int64_t hq = std::max<int32_t>(num_q_heads, 1);
+    const int64_t rmin = std::max<int64_t>(1, kPrefillQRows / hq);
+    const int64_t blocks = toks / rmin + seqs;
+    const int64_t prefill_units = blocks * kPrefillMaxPieces * hq;
     const int64_t units = nq + seqs + prefill_units;
     const int64_t merges = seqs + blocks;
     const int64_t prows = nq + seqs + toks * kPrefillMaxPieces;

@@ -105,25 +105,31 @@ def test_mixed_plan_covers_every_visible_pair_once():
     units, qoff, merges = pkv.decode_plan_image(p, image)
     cu = np.concatenate([[0], np.cumsum(ql)])
     assert p.num_tokens == cu[-1] and p.max_q_len == 700
+    hkv = 8
     for s in range(len(lens)):
         n, L = int(lens[s]), int(ql[s])
-        cover = np.zeros((L, n), np.int32)
+        heads = hkv if L > 1 else 1  # a prefill unit holds one kv head, a decode unit all of them
+        cover = np.zeros((heads, L, n), np.int32)
         for u in units[units[:, 0] == s]:
             seq, kb, ke, row0, nrows, pos0, prow, kind = (int(x) for x in u)
-            assert kind == (1 if L > 1 else 0)
+            assert (1 <= kind <= hkv) if L > 1 else kind == 0
+            assert kb < ke
             r = row0 - cu[s]
             assert pos0 == n - L + r
             for i in range(nrows):
                 pos = pos0 + i
                 lo, hi = kb, min(ke, pos + 1)
                 if hi > lo:
-                    cover[r + i, lo:hi] += 1
+                    cover[max(kind - 1, 0), r + i, lo:hi] += 1
         visible = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]
-        assert np.array_equal(cover, visible.astype(np.int32)), s
+        assert np.array_equal(cover, np.broadcast_to(visible.astype(np.int32), cover.shape)), s
     # every merged block lists its pieces at prow0 + c * nrows
     for row0, nrows, prow0, parts in merges:
         us = units[(units[:, 3] == row0) & (units[:, 6] >= 0)]
-        assert sorted(us[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
+        for kind in sorted(set(us[:, 7].tolist())):
+            mine = us[us[:, 7] == kind]
+            assert sorted(mine[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
+        assert len(us) == parts * (hkv if us[0, 7] >= 1 else 1)
 
 
 def test_workspace_bound_covers_plans():
