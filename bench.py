@@ -1,23 +1,31 @@
 #!/usr/bin/env python3
-"""Benchmark: paged decode attention on one MI355X.
+"""Benchmark: paged KV attention on one MI355X.
 
-One step = one decode step of a Qwen3-4B-shaped model's attention: the
-split-KV plan once on the host, then for each of the 36 layers the write of
-this step's K/V (64 new tokens) and the paged decode over that layer's own
-pool (64 sequences, context uniform in [512, 4096], 32 query / 8 KV heads,
-head dim 128, page 16, bf16).  The plan is made once per step and reused by
-every layer, as the planner's description on "How Easy Is It to Start Serving
-LLMs?" (Phase 4 §3) has it.
+Default workload (``--config decode``): one decode step of a Qwen3-4B-shaped
+model's attention: the split-KV plan once on the host, then for each of the
+36 layers the write of this step's K/V (64 new tokens) and the paged decode
+over that layer's own pool (64 sequences, context uniform in [512, 4096], 32
+query / 8 KV heads, head dim 128, page 16, bf16).  The plan is made once per
+step and reused by every layer, as the planner's description on "How Easy Is
+It to Start Serving LLMs?" (Phase 4 §3) has it.  Other workloads:
+``long-page1`` / ``long-page16`` / ``long-contig`` (16 x 32768 keys, the
+scattered-vs-contiguous comparison), ``fp8prefix`` (128 sequences over a
+shared 4096-token prefix, fp8 cache), ``mixed`` (63 decodes and one 512-row
+prefill chunk packed in one step; "nanoserve" chunked prefill) and
+``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
+peak).
 
 Inputs are synthetic: block tables, lengths and slots come from the seeded
 generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
-seeded torch generator per layer and rounded to bf16.  They are resident in
-HBM before timing starts.
+seeded torch generator per layer and rounded to bf16 (fp8: quantised by the
+library's own write).  They are resident in HBM before timing starts.
 
 Printed: one JSON line.  ``value`` is the step's algorithmic bytes (every
 valid K/V element, q, out, table entries, lengths, and the write's bytes) over
-its wall time, in TB/s.  ``roofline`` covers the dominant call,
-paged_attn_decode, timed with HIP events around every call on its stream.
+its wall time, in TB/s.  ``roofline`` covers the dominant call (the attention
+call: its kernel and the merge kernel), timed with HIP events around every
+call on its stream; with prefill chunks in the step it reads the chunk's
+flops against the bf16 matrix-core peak when that fraction is the larger.
 ``cpu_baseline`` is the fp64 CPU oracle (write + attention of layer 0) timed
 on this host's cores.
 """
@@ -45,7 +53,13 @@ CONFIGS = {
     "long-page16": dict(config="long", layout="page16", desc="16 seqs x 32768, 32q/8kv, D=128, page 16 shuffled, bf16"),
     "long-contig": dict(config="long", layout="contig", desc="16 seqs x 32768, 32q/8kv, D=128, contiguous slab, bf16"),
     "fp8prefix": dict(config="fp8prefix", layout="page16", desc="128 seqs, 4096 shared + 256 private tokens, fp8 E4M3 KV"),
+    "mixed": dict(config="mixed", layout="page16",
+                  desc="63 decodes (ctx U[256,2048]) + one 512-row chunk over 2048 cached tokens, packed T=575, "
+                       "32q/8kv, D=128, page 16, bf16"),
+    "mixed-chunk": dict(config="mixed", layout="page16", only_chunk=True,
+                        desc="the 512-row chunk of the mixed step alone (2560 keys, causal), 32q/8kv, D=128, bf16"),
 }
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 
 
 def log(msg):
@@ -58,7 +72,7 @@ def build_layers(torch, st, cfg, layers, dev):
 
     hq, hkv, d = 32, 8, 128
     nb, bs = st["num_blocks"], st["block_size"]
-    B = st["context_lens"].shape[0]
+    B = int(st["q_lens"].sum())  # query rows (one per sequence for decode)
     fp8 = cfg["config"] == "fp8prefix"
     out = []
     for l in range(layers):
@@ -114,7 +128,8 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
     q, kn, vn = host(layer["q"]), host(layer["k_new"]), host(layer["v_new"])
     ks, vs = scales
     B = st["context_lens"].shape[0]
-    cu = np.arange(B + 1, dtype=np.int32)
+    T = int(st["q_lens"].sum())
+    cu = st["cu_seqlens"]
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
     reps, t0 = 0, time.perf_counter()
     while True:
@@ -127,8 +142,8 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
             break
     per = el / reps
     kvb = 1 if kv_dtype == "fp8" else 2
-    nbytes = byte_model.attention_bytes(st["context_lens"], np.ones(B), 32, 8, 128, st["block_size"], kvb, 2) + \
-        byte_model.write_bytes(B, 8, 128, 2, kvb)
+    nbytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2) + \
+        byte_model.write_bytes(T, 8, 128, 2, kvb)
     try:
         from threadpoolctl import threadpool_info
 
@@ -138,7 +153,7 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
     cores = len(os.sched_getaffinity(0))
     return {"value": nbytes / per / 1e12, "unit": "TB/s", "cores": int(blas or cores),
             "kind": "oracle", "host_cores": cores, "seconds_per_layer_call": per,
-            "sample": f"layer 0 of the step (write of {B} tokens + attention of all {B} sequences), "
+            "sample": f"layer 0 of the step (write of {T} tokens + attention of all {B} sequences), "
                       f"{reps} repetition(s), fp64 NumPy oracle", "out": out}
 
 
@@ -225,7 +240,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     st = workloads.structure_only(cfg["config"], cfg["layout"])
+    if cfg.get("only_chunk"):
+        s_ = int(np.argmax(st["q_lens"]))
+        L = int(st["q_lens"][s_])
+        cu0 = int(st["cu_seqlens"][s_])
+        st = dict(st, context_lens=st["context_lens"][s_:s_ + 1], q_lens=st["q_lens"][s_:s_ + 1],
+                  cu_seqlens=np.array([0, L], np.int32), block_tables=st["block_tables"][s_:s_ + 1],
+                  slot_mapping=st["slot_mapping"][cu0:cu0 + L])
     B = st["context_lens"].shape[0]
+    T = int(st["q_lens"].sum())
+    mixed = bool(np.any(st["q_lens"] > 1))
     kv_dtype = "fp8" if cfg["config"] == "fp8prefix" else "bf16"
     kvb = 1 if kv_dtype == "fp8" else 2
     log(f"building {args.layers} layers of {args.config}")
@@ -236,13 +260,18 @@ def main():
     tables = torch.from_numpy(st["block_tables"]).to(dev)
     ctx = torch.from_numpy(st["context_lens"]).to(dev)
     slots = torch.from_numpy(st["slot_mapping"]).to(dev)
+    cu = torch.from_numpy(st["cu_seqlens"]).to(dev)
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
-    plan = pkv.Plan(st["context_lens"], num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev)
+    q_lens = st["q_lens"] if mixed else None
+    plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    attn_bytes = byte_model.attention_bytes(st["context_lens"], np.ones(B), 32, 8, 128, st["block_size"], kvb, 2)
-    wr_bytes = byte_model.write_bytes(B, 8, 128, 2, kvb)
+    attn_bytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2)
+    attn_flops = byte_model.attention_flops(st["context_lens"], st["q_lens"], 32, 128)
+    chunk = st["q_lens"] > 1
+    chunk_flops = byte_model.attention_flops(st["context_lens"][chunk], st["q_lens"][chunk], 32, 128)
+    wr_bytes = byte_model.write_bytes(T, 8, 128, 2, kvb)
     step_bytes = args.layers * (attn_bytes + wr_bytes)
 
     n_events = args.steps * args.layers
@@ -252,14 +281,19 @@ def main():
 
     def step(timed_index=None):
         t0 = time.perf_counter()
-        plan.update(st["context_lens"])
+        plan.update(st["context_lens"], q_lens)
         plan_s.append(time.perf_counter() - t0)
         for l, layer in enumerate(layers):
             ks, vs = scales[l]
             pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
             if timed_index is not None:
                 ev_a[timed_index * args.layers + l].record(stream)
-            pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan, ks, vs)
+            if mixed:
+                pkv.paged_attn_mixed(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, cu, ctx, scale, plan,
+                                     ks, vs)
+            else:
+                pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan,
+                                      ks, vs)
             if timed_index is not None:
                 ev_b[timed_index * args.layers + l].record(stream)
 
@@ -277,8 +311,23 @@ def main():
     decode_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e12
-    dec_avg_s = float(decode_ms.mean()) / 1e3
-    achieved = attn_bytes / dec_avg_s / 1e12
+    call_s = float(decode_ms.mean()) / 1e3
+    hbm_frac = attn_bytes / call_s / (PEAK_HBM_TBS * 1e12)
+    mfma_tflops = chunk_flops / call_s / 1e12
+    mfma_frac = mfma_tflops / PEAK_BF16_TFLOPS
+    call_name = ("paged_attn_mixed (mixed kernel + merge kernel, one call)" if mixed else
+                 "paged_attn_decode (decode-unit kernel + merge kernel, one call)")
+    if mixed and mfma_frac > hbm_frac:
+        roofline = {"bound": "mfma", "kernel": call_name, "achieved": round(mfma_tflops, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
+                    "flops_per_launch": int(chunk_flops), "traffic": None}
+    else:
+        roofline = {"bound": "hbm", "kernel": call_name, "achieved": round(attn_bytes / call_s / 1e9, 2),
+                    "peak": PEAK_HBM_TBS * 1e3, "unit": "GB/s", "frac": round(hbm_frac, 4),
+                    "bytes_per_launch": int(attn_bytes), "traffic": None}
+    if mixed:
+        roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+                             "chunk_tflops": round(mfma_tflops, 2)}
 
     result = {
         "metric": METRIC,
@@ -294,30 +343,22 @@ def main():
         "dtype": kv_dtype,
         "data": "synthetic: seeded N(0,1) K/V/Q, seeded lengths and shuffled block tables",
         "config": {
-            "workload": f"{args.config}: {cfg['desc']}; one step = plan + {args.layers} layers x (write + decode)",
+            "workload": f"{args.config}: {cfg['desc']}; one step = plan + {args.layers} layers x (write + attention)",
             "num_seqs": int(B),
+            "query_rows": int(T),
             "total_context_tokens": int(st["context_lens"].sum()),
             "layers": args.layers,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_TBS, 2),
         "us_per_layer": round(ms_step * 1e3 / args.layers, 3),
-        "decode_call_us": {"mean": round(float(decode_ms.mean()) * 1e3, 3),
-                           "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 3),
-                           "p50": round(float(np.median(decode_ms)) * 1e3, 3),
-                           "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 3)},
+        "attention_call_us": {"mean": round(float(decode_ms.mean()) * 1e3, 3),
+                              "p10": round(float(np.percentile(decode_ms, 10)) * 1e3, 3),
+                              "p50": round(float(np.median(decode_ms)) * 1e3, 3),
+                              "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 3)},
         "plan_us_per_step": round(float(np.median(plan_s)) * 1e6, 2),
         "plan_us_per_layer": round(float(np.median(plan_s)) * 1e6 / args.layers, 3),
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "paged_attn_decode (decode-unit kernel + merge kernel, one call)",
-            "achieved": round(achieved * 1e3, 2),
-            "peak": PEAK_HBM_TBS * 1e3,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_TBS, 4),
-            "bytes_per_launch": int(attn_bytes),
-            "traffic": None,
-        },
+        "roofline": roofline,
         "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
                  "merges": int(plan.desc.num_merges), "target_tiles": int(plan.desc.target_tiles)},
     }

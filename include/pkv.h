@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /* Status codes. */
 #define PKV_OK 0
@@ -95,12 +95,14 @@ typedef struct pkv_plan {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
-    int32_t num_queues;       /* workgroups of the attention launch */
-    int32_t num_units;        /* pieces of work */
+    int32_t num_queues;       /* workgroups of the decode launch */
+    int32_t num_units;        /* pieces of work (decode and prefill) */
     int32_t num_merges;       /* groups of rows whose pieces are merged */
     int32_t num_partial_rows; /* rows of partial results in the workspace */
     int32_t target_tiles;     /* ideal work per queue, in 16-token tiles */
     int32_t max_q_len;
+    int32_t num_prefill_queues; /* workgroups of the prefill launch (0: no chunk rows) */
+    int32_t num_prefill_units;  /* of num_units; they sit after the decode units */
     int64_t off_units;        /* byte offsets inside the workspace */
     int64_t off_queues;
     int64_t off_merges;
@@ -110,7 +112,7 @@ typedef struct pkv_plan {
     int64_t workspace_bytes;  /* bytes of workspace the plan uses */
 } pkv_plan;
 
-#define PKV_PLAN_MAGIC 0x504b5631 /* "PKV1" */
+#define PKV_PLAN_MAGIC 0x504b5632 /* "PKV2" */
 
 /* Text of a status code; never NULL. */
 const char* paged_attn_strerror(int status);
@@ -235,10 +237,17 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
  * paged_attn_mixed - a packed batch: sequence s owns query rows
  * cu_seqlens[s] .. cu_seqlens[s+1]-1 of q and out (num_tokens rows in all);
  * row i of its L rows attends causally to keys 0 .. n - L + i of its
- * n = context_lens[s] keys.  Rows of one-row sequences take the decode
- * path; chunks take a tiled path whose QK^T and PV products run on the
- * matrix cores.  Same arguments and errors as paged_attn_decode, with the
- * plan made from the same q_lens.
+ * n = context_lens[s] keys.  Two launches on `stream`: the decode kernel
+ * for the rows of one-row sequences (the plan's decode queues) and a tiled
+ * kernel for the chunks (its prefill queues), whose QK^T and PV products run
+ * on the matrix cores with P rounded to bf16; then one merge of cut pieces.
+ * Same arguments and errors as paged_attn_decode, with the plan made from
+ * the same q_lens, plus: PKV_ERR_UNSUPPORTED when the plan has chunk rows
+ * and q is not bf16 (K/V bf16 or fp8; decode-only plans take every dtype
+ * paged_attn_decode takes), PKV_ERR_SHAPE when chunk rows meet a cache not
+ * aligned to 8 elements.  A block id outside the pool turns the rows of
+ * every unit that reads it into NaN (a unit holds up to 128 / G rows of one
+ * chunk) and is never dereferenced.
  * ("nanoserve", "Packed batches" and chunked-prefill bullets, and the
  * benchmark note on splitting each mixed step into decode rows and prefill
  * chunks; "How to design an LLM serving system", "Latency and scaling

@@ -31,7 +31,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 
-PLAN_MAGIC = 0x504B5631
+PLAN_MAGIC = 0x504B5632
 
 # Symbols include/pkv.h declares (checked by the CPU tests).
 EXPORTS = (
@@ -61,6 +61,8 @@ class PkvPlan(ctypes.Structure):
         ("num_partial_rows", ctypes.c_int32),
         ("target_tiles", ctypes.c_int32),
         ("max_q_len", ctypes.c_int32),
+        ("num_prefill_queues", ctypes.c_int32),
+        ("num_prefill_units", ctypes.c_int32),
         ("off_units", ctypes.c_int64),
         ("off_queues", ctypes.c_int64),
         ("off_merges", ctypes.c_int64),
@@ -205,10 +207,11 @@ MERGE_FIELDS = ("row0", "nrows", "prow0", "parts")
 
 
 def decode_plan_image(p: PkvPlan, image: np.ndarray):
-    """Split a plan image into (units [U, 8], queue offsets [Q+1], merges [M, 4]) int32 arrays."""
+    """Split a plan image into (units [U, 8], queue offsets [Q + Qp + 1], merges [M, 4])
+    int32 arrays; decode queues come first, then the Qp prefill queues."""
     b = np.asarray(image, dtype=np.uint8)
     units = b[p.off_units:p.off_units + 32 * p.num_units].view(np.int32).reshape(-1, 8)
-    queues = b[p.off_queues:p.off_queues + 4 * (p.num_queues + 1)].view(np.int32)
+    queues = b[p.off_queues:p.off_queues + 4 * (p.num_queues + p.num_prefill_queues + 1)].view(np.int32)
     merges = b[p.off_merges:p.off_merges + 16 * p.num_merges].view(np.int32).reshape(-1, 4)
     return units, queues, merges
 

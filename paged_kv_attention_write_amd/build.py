@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_plan.cpp", "pkv_api.cpp", "pkv_write.hip", "pkv_decode.hip", "pkv_mixed.hip"]
+SOURCES = ["pkv_plan.cpp", "pkv_api.cpp", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip"]
 
 COMMON = [
     "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",

@@ -1,6 +1,7 @@
 // C ABI: argument checks, the plan upload and kernel launches.  Every check
 // runs on the host before anything is launched; a failing check returns a
 // negative status and leaves device memory untouched.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -218,7 +219,13 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
     st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
     if (st != PKV_OK) return st;
     const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, q_dtype, head_dim, stream);
+    return launch_merge(a, merges, plan->num_merges, 1, q_dtype, head_dim, stream);
+}
+
+// Most rows of any merge record: decode merges have one, prefill merges a row block.
+static int merge_rows(const pkv_plan* plan, int group) {
+    if (plan->num_prefill_units == 0) return 1;
+    return std::max(1, std::min(plan->max_q_len, std::max(1, kPrefillQRows / group)));
 }
 
 int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
@@ -238,13 +245,23 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
     const AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
                                  max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, num_blocks, block_size,
                                  scale, k_scale, v_scale, plan, workspace);
-    if (plan->max_q_len <= 1)
-        st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
-    else
-        st = launch_mixed(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
-    if (st != PKV_OK) return st;
+    const int group = num_q_heads / num_kv_heads;
+    const bool chunks = plan->num_prefill_units > 0;
+    if (chunks && !prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    // the prefill tile stages 8 elements of a key per load
+    const size_t item = 8 * static_cast<size_t>(dt_bytes(kv_dtype));
+    if (chunks && (!aligned(k_cache, item) || !aligned(v_cache, item))) return PKV_ERR_SHAPE;
+    if (plan->num_units > plan->num_prefill_units) {
+        st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
+        if (st != PKV_OK) return st;
+    }
+    if (chunks) {
+        st = launch_prefill(a, q_dtype, kv_dtype, head_dim, group, plan->num_prefill_queues, plan->num_queues,
+                            stream);
+        if (st != PKV_OK) return st;
+    }
     const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, q_dtype, head_dim, stream);
+    return launch_merge(a, merges, plan->num_merges, merge_rows(plan, group), q_dtype, head_dim, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,8 @@ void decode_kernel(AttnArgs a) {
 // Merge of the partial results of cut sequences.  One wave per (merge record,
 // row, head): lane c reads part c's lse (log2 units), a wave max and sum give
 // the part weights w_c = 2^(lse_c - M) / sum, then every lane accumulates its
-// D/64 elements over the parts with independent loads.
+// D/64 elements over the parts with independent loads.  Grid: (merge record,
+// row of the record, group of kMergeWaves heads).
 constexpr int kMergeWaves = 4;
 
 template <int QDT, int D>
@@ -35,11 +36,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
                                                                  void* __restrict__ out, int hq, float v_scale) {
     constexpr int E = D / 64;  // elements per lane
     const Merge mg = merges[blockIdx.x];
+    const int r = blockIdx.y;
     const int lane = threadIdx.x & 63;
-    const int h = blockIdx.y * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (h >= hq) return;
+    const int h = blockIdx.z * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (h >= hq || r >= mg.nrows) return;
     const int64_t hd = static_cast<int64_t>(hq) * D;
-    for (int r = 0; r < mg.nrows; ++r) {
+    {
         // weights of the parts, 64 at a time
         float M = -INFINITY;
         bool nan = false;
@@ -157,10 +159,11 @@ int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, in
     return PKV_ERR_UNSUPPORTED;
 }
 
-int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int q_dtype, int head_dim, void* stream) {
+int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int max_rows, int q_dtype, int head_dim,
+                 void* stream) {
     if (num_merges == 0) return PKV_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(num_merges, (a.hq + kMergeWaves - 1) / kMergeWaves);
+    const dim3 grid(num_merges, max_rows, (a.hq + kMergeWaves - 1) / kMergeWaves);
     const dim3 block(kMergeWaves * 64);
     if (q_dtype == PKV_DTYPE_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_F32, 64>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,

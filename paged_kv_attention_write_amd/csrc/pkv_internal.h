@@ -16,9 +16,11 @@ constexpr int kTileTokens = 16;
 // rows of a chunk are taken in blocks of kPrefillQRows / G rows (G = q heads
 // per kv head), each block times each kv head times each key piece.
 constexpr int kPrefillQRows = 128;
-// Key pieces of one prefill row block: at most this many.  A piece is cut so
-// that its cost stays within one queue's share of the step.
+// Key pieces of one prefill row block: at most this many, each at least
+// kPrefillPieceMin keys (the last may be shorter).  Within those limits a
+// piece is cut so that its cost stays within one prefill queue's share.
 constexpr int kPrefillMaxPieces = 8;
+constexpr int kPrefillPieceMin = 512;
 // Cost of a prefill unit in decode tiles: one tile of decode work (16 keys of
 // 8 kv heads x 128 dims in bf16, 64 KiB) takes a queue about as long as this
 // many flops of matrix-core work.

@@ -10,11 +10,12 @@
 // only where a queue fills up (at most queues + requests pieces in all).
 //
 // Query chunks (more than one new row) are split into blocks of rows, one
-// unit per (row block, kv head, key piece); a unit's cost is its matrix-core
-// work expressed in tiles, the key range of a row block is cut so that no
-// piece costs more than the share, and these units are placed before the
-// decode requests, largest first.
-// before the decode requests, largest first.
+// unit per (row block, kv head, key piece), and run as a launch of their own
+// over a second set of queues: a unit's cost is its matrix-core work
+// expressed in tiles, the key range of a row block is cut so that a piece
+// stays within that launch's share, and the units are placed largest first,
+// each whole on the least-loaded prefill queue.
+
 #include <algorithm>
 #include <cstring>
 #include <queue>
@@ -103,9 +104,12 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         if (L == 1) decode_tiles += ceil_div(n, kTileTokens);
         if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
     }
-    // first share: cuts the key ranges of the prefill row blocks
-    const int64_t total0 = decode_tiles + ceil_div(prefill_flops, kFlopsPerTile);
-    const int64_t target0 = total0 > 0 ? ceil_div(total0, num_queues) : 0;
+    // Decode rows and prefill chunks run as two launches over the same
+    // number of queues, each balanced on its own.  The prefill share cuts
+    // the key ranges of the prefill row blocks.
+    const int32_t prefill_queues = prefill_flops > 0 ? num_queues : 0;
+    const int64_t prefill_tiles = ceil_div(prefill_flops, kFlopsPerTile);
+    const int64_t target0 = prefill_queues > 0 ? ceil_div(prefill_tiles, prefill_queues) : 0;
 
     // Prefill units: row blocks x kv heads x key pieces of every chunk.
     std::vector<PrefillPiece> prefill;
@@ -121,7 +125,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int32_t extent = n - L + r1;  // keys the last row of the block sees
             // tiles of the longest piece whose full-width cost fits the share
             const int64_t per_tile = static_cast<int64_t>(nr) * flops_per_pair * kTileTokens;
-            const int64_t fit = std::max<int64_t>(1, target0 * kFlopsPerTile / per_tile);
+            const int64_t fit =
+                std::max<int64_t>(kPrefillPieceMin / kTileTokens, target0 * kFlopsPerTile / per_tile);
             const int64_t want = ceil_div(ceil_div(extent, kTileTokens), fit);
             const int64_t ask = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, want));
             const int64_t piece = ceil_div(ceil_div(extent, ask), kTileTokens) * kTileTokens;
@@ -145,25 +150,24 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         }
     }
 
-    // The share of the placement: the units' own (rounded) costs plus the
-    // decode tiles, so that the queues together hold exactly the total and a
-    // queue below the share exists while any work is left.
-    int64_t total = decode_tiles;
-    for (const auto& p : prefill) total += p.cost;
-    const int64_t target = total > 0 ? ceil_div(total, num_queues) : 0;
+    // Prefill units, largest first, each whole on the least-loaded prefill queue.
+    std::vector<std::vector<Unit>> pqueues(static_cast<size_t>(prefill_queues));
+    if (prefill_queues > 0) {
+        QueueHeap pheap(prefill_queues);
+        std::stable_sort(prefill.begin(), prefill.end(), [](const PrefillPiece& a, const PrefillPiece& b) {
+            return a.cost > b.cost;
+        });
+        for (const auto& p : prefill) {
+            auto [load, q] = pheap.pop();
+            pqueues[q].push_back(p.unit);
+            pheap.push(load + p.cost, q);
+        }
+    }
 
+    // The decode share: the decode tiles over the queues.
+    const int64_t target = decode_tiles > 0 ? ceil_div(decode_tiles, num_queues) : 0;
     std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
     QueueHeap heap(num_queues);
-
-    // Whole prefill units, largest first.
-    std::stable_sort(prefill.begin(), prefill.end(), [](const PrefillPiece& a, const PrefillPiece& b) {
-        return a.cost > b.cost;
-    });
-    for (const auto& p : prefill) {
-        auto [load, q] = heap.pop();
-        queues[q].push_back(p.unit);
-        heap.push(load + p.cost, q);
-    }
 
     // Decode requests, longest first, cut to fill the lightest queue.
     std::vector<int32_t> order;
@@ -200,11 +204,16 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
 
     int64_t num_units = 0;
     for (const auto& q : queues) num_units += static_cast<int64_t>(q.size());
+    const int64_t num_prefill_units = static_cast<int64_t>(prefill.size());
+    num_units += num_prefill_units;
     if (num_units > INT32_MAX || partial_rows > INT32_MAX) return PKV_ERR_SHAPE;
 
-    // Image: [units][queue offsets][merges], then the partial results.
+    // Image: [units][queue offsets][merges], then the partial results.  The
+    // decode queues' units come first, then the prefill queues'; the queue
+    // offsets run over both (num_queues + prefill_queues + 1 entries).
     const size_t units_bytes = align_up(static_cast<size_t>(num_units) * sizeof(Unit));
-    const size_t queues_bytes = align_up((static_cast<size_t>(num_queues) + 1) * sizeof(int32_t));
+    const size_t queues_bytes =
+        align_up((static_cast<size_t>(num_queues) + static_cast<size_t>(prefill_queues) + 1) * sizeof(int32_t));
     const size_t merges_bytes = align_up(merges.size() * sizeof(Merge));
     const size_t image = units_bytes + queues_bytes + merges_bytes;
     const size_t po_bytes = align_up(static_cast<size_t>(partial_rows) * static_cast<size_t>(hd) * sizeof(float));
@@ -222,6 +231,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     plan->num_partial_rows = static_cast<int32_t>(partial_rows);
     plan->target_tiles = static_cast<int32_t>(std::min<int64_t>(target, INT32_MAX));
     plan->max_q_len = max_q;
+    plan->num_prefill_queues = prefill_queues;
+    plan->num_prefill_units = static_cast<int32_t>(num_prefill_units);
     plan->off_units = 0;
     plan->off_queues = static_cast<int64_t>(units_bytes);
     plan->off_merges = static_cast<int64_t>(units_bytes + queues_bytes);
@@ -244,7 +255,11 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         qoff[q] = cursor;
         for (const Unit& x : queues[q]) u[cursor++] = x;
     }
-    qoff[num_queues] = cursor;
+    for (int32_t q = 0; q < prefill_queues; ++q) {
+        qoff[num_queues + q] = cursor;
+        for (const Unit& x : pqueues[q]) u[cursor++] = x;
+    }
+    qoff[num_queues + prefill_queues] = cursor;
     if (!merges.empty())
         std::memcpy(base + units_bytes + queues_bytes, merges.data(), merges.size() * sizeof(Merge));
     plan->magic = PKV_PLAN_MAGIC;
@@ -267,7 +282,7 @@ void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int3
     const int64_t merges = seqs + blocks;
     const int64_t prows = nq + seqs + toks * kPrefillMaxPieces;
     const size_t image = align_up(static_cast<size_t>(units) * sizeof(Unit)) +
-                         align_up(static_cast<size_t>(nq + 1) * sizeof(int32_t)) +
+                         align_up(static_cast<size_t>(2 * nq + 1) * sizeof(int32_t)) +
                          align_up(static_cast<size_t>(merges) * sizeof(Merge));
     const size_t hd = static_cast<size_t>(std::max(num_q_heads, 1)) * static_cast<size_t>(std::max(head_dim, 1));
     const size_t po = align_up(static_cast<size_t>(prows) * hd * sizeof(float));

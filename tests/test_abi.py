@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.pkv_abi_version() == 1
+    assert L.pkv_abi_version() == 2
 
 
 def test_strerror_covers_all_codes():
@@ -130,6 +130,32 @@ def test_mixed_plan_covers_every_visible_pair_once():
             mine = us[us[:, 7] == kind]
             assert sorted(mine[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
         assert len(us) == parts * (hkv if us[0, 7] >= 1 else 1)
+
+
+def test_mixed_plan_decode_queues_equal_the_decode_plan():
+    """Decode rows of a mixed step are placed exactly as a decode-only plan of
+    those sequences would place them; chunk units sit on the prefill queues."""
+    lens, ql = _mixed_case()
+    nq = 96
+    p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
+    units, qoff, _ = pkv.decode_plan_image(p, image)
+    assert p.num_prefill_queues == nq and len(qoff) == 2 * nq + 1
+    dec = np.nonzero(ql == 1)[0]
+    want = split_kv_plan(lens[dec].tolist(), nq)
+    got = [[(int(dec.tolist().index(u[0])), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]]
+           for q in range(nq)]
+    assert got == want
+    pre = units[qoff[nq]:qoff[2 * nq]]
+    assert len(pre) == p.num_prefill_units and np.all(pre[:, 7] >= 1)
+    assert np.all(units[:qoff[nq], 7] == 0)
+    assert qoff[2 * nq] == p.num_units
+
+
+def test_decode_only_plan_has_no_prefill_queues():
+    lens = np.array([100, 2000, 5], np.int32)
+    p, image = pkv.plan_host(lens, None, 32, 8, 128, 16)
+    units, qoff, _ = pkv.decode_plan_image(p, image)
+    assert p.num_prefill_queues == 0 and p.num_prefill_units == 0 and len(qoff) == 17
 
 
 def test_workspace_bound_covers_plans():
