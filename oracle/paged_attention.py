@@ -16,7 +16,7 @@ architecture diagram; "How to design an LLM serving system", "PagedAttention"):
   write (each layer writes first, then attends over the whole context:
   "nanoserve", "One engine step", step 3).
 
-Readings of points the pages leave open (each is also listed in the design doc):
+Readings of points the pages leave open:
 
 * GQA groups are consecutive: q head ``h`` reads kv head ``h // (Hq / H_kv)``.
 * A chunk of ``L`` new rows over a context of ``n`` keys is aligned at the

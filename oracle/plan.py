@@ -8,7 +8,7 @@ pieces no longer than that ideal share, and gives every piece to the queue
 with the least work so far.  Every layer of the step reuses the plan; a merge
 step joins the pieces of a request that was cut.
 
-Readings of what the illustration leaves open (listed in the design doc too):
+Readings of what the illustration leaves open:
 
 * Work is counted in 16-token tiles, the granularity the kernels walk the
   cache in; a request of ``n`` tokens is ``ceil(n / 16)`` tiles, and every

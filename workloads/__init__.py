@@ -5,7 +5,7 @@ holds no arithmetic of the method: it draws random numbers, rounds them to the
 storage dtype of the inputs, builds block tables, slot lists and packed-token
 offsets, and nothing else.  Neither the oracle nor the GPU library imports it.
 
-Shapes follow the pages' workloads (each recipe is restated in the design doc):
+Shapes follow the pages' workloads:
 
 * ``tiny``      - 4 sequences of 7/16/33/100 keys, 4 q / 2 kv heads, D=64,
   page 16, a 64-block pool in seeded random order, fp32.
