@@ -203,10 +203,16 @@ def copy_calibration(torch):
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(3):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(3):
         dst.copy_(src)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "dispatches": 3}), flush=True)
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(3)]
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "dispatches": 3,
+                      "copy_ms": ms, "copy_read_plus_write_TBps": [2 * COPY_BYTES / (m * 1e-3) / 1e12 for m in ms]}),
+          flush=True)
 
 
 def main():
@@ -218,6 +224,7 @@ def main():
     ap.add_argument("--config", default="decode", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--queues", type=int, default=0, help="planner queues (0: the library default, 2 per CU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -263,7 +270,8 @@ def main():
     cu = torch.from_numpy(st["cu_seqlens"]).to(dev)
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
     q_lens = st["q_lens"] if mixed else None
-    plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev)
+    plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                    num_queues=args.queues)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 

@@ -161,7 +161,10 @@ int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int6
 int paged_attn_workspace_size(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
                               int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes);
 
-/* Default number of attention workgroups (queues) on the current device. */
+/*
+ * Default number of decode workgroups (queues) on the current device: one per
+ * compute unit.  A plan with chunk rows adds two prefill queues per queue.
+ */
 int paged_attn_default_queues(int32_t* num_queues);
 
 /*

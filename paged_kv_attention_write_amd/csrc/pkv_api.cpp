@@ -15,9 +15,12 @@ namespace {
 using namespace pkv;
 
 constexpr float kLog2e = 1.4426950408889634f;
-// Persistent attention workgroups per compute unit (two 8-wave workgroups
-// fill 16 wave slots of a CU at <= 128 VGPRs per lane).
-constexpr int kQueuesPerCU = 2;
+// Persistent decode workgroups per compute unit.  One workgroup per CU
+// streams fastest for bf16 on whole-tile pages (measured against two and
+// more); the kernels that need more waves in flight (page sizes that are not
+// a multiple of 16, fp8) use 16-wave workgroups instead, and the prefill
+// launch takes two queues per decode queue.
+constexpr int kQueuesPerCU = 1;
 
 bool dtype_ok(int32_t dt) { return dt == PKV_DTYPE_F32 || dt == PKV_DTYPE_BF16 || dt == PKV_DTYPE_FP8_E4M3; }
 

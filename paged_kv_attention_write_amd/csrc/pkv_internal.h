@@ -17,10 +17,13 @@ constexpr int kTileTokens = 16;
 // per kv head), each block times each kv head times each key piece.
 constexpr int kPrefillQRows = 128;
 // Key pieces of one prefill row block: at most this many, each at least
-// kPrefillPieceMin keys (the last may be shorter).  Within those limits a
-// piece is cut so that its cost stays within one prefill queue's share.
+// kPrefillPieceMin keys (the last may be shorter).  Within those limits a row
+// block gets pieces in proportion to its share of the chunks' work.
 constexpr int kPrefillMaxPieces = 8;
 constexpr int kPrefillPieceMin = 512;
+// Prefill queues per decode queue: the prefill kernel runs two 8-wave
+// workgroups per CU when the decode launch runs one.
+constexpr int kPrefillQueuesPerQueue = 2;
 // Cost of a prefill unit in decode tiles: one tile of decode work (16 keys of
 // 8 kv heads x 128 dims in bf16, 64 KiB) takes a queue about as long as this
 // many flops of matrix-core work.

@@ -11,10 +11,11 @@
 //
 // Query chunks (more than one new row) are split into blocks of rows, one
 // unit per (row block, kv head, key piece), and run as a launch of their own
-// over a second set of queues: a unit's cost is its matrix-core work
-// expressed in tiles, the key range of a row block is cut so that a piece
-// stays within that launch's share, and the units are placed largest first,
-// each whole on the least-loaded prefill queue.
+// over a second set of queues: the key range of a row block is cut into as
+// many pieces as its share of the chunks' work is of those queues, so that
+// the units fill them about once; a unit's cost is its matrix-core work
+// expressed in tiles, and the units are placed largest first, each whole on
+// the least-loaded prefill queue.
 
 #include <algorithm>
 #include <cstring>
@@ -104,12 +105,9 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         if (L == 1) decode_tiles += ceil_div(n, kTileTokens);
         if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
     }
-    // Decode rows and prefill chunks run as two launches over the same
-    // number of queues, each balanced on its own.  The prefill share cuts
-    // the key ranges of the prefill row blocks.
-    const int32_t prefill_queues = prefill_flops > 0 ? num_queues : 0;
-    const int64_t prefill_tiles = ceil_div(prefill_flops, kFlopsPerTile);
-    const int64_t target0 = prefill_queues > 0 ? ceil_div(prefill_tiles, prefill_queues) : 0;
+    // Decode rows and prefill chunks run as two launches, each balanced on
+    // its own queues.
+    const int32_t prefill_queues = prefill_flops > 0 ? kPrefillQueuesPerQueue * num_queues : 0;
 
     // Prefill units: row blocks x kv heads x key pieces of every chunk.
     std::vector<PrefillPiece> prefill;
@@ -123,12 +121,16 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int32_t r1 = std::min(L, r0 + block_rows);
             const int32_t nr = r1 - r0;
             const int32_t extent = n - L + r1;  // keys the last row of the block sees
-            // tiles of the longest piece whose full-width cost fits the share
-            const int64_t per_tile = static_cast<int64_t>(nr) * flops_per_pair * kTileTokens;
-            const int64_t fit =
-                std::max<int64_t>(kPrefillPieceMin / kTileTokens, target0 * kFlopsPerTile / per_tile);
-            const int64_t want = ceil_div(ceil_div(extent, kTileTokens), fit);
-            const int64_t ask = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, want));
+            // pieces per kv head: the row block's share of the prefill queues
+            // (its work over the chunks' total), so that the chunk units fill
+            // the prefill queues about once; at least one, at most
+            // kPrefillMaxPieces, none shorter than kPrefillPieceMin keys
+            const int64_t block_flops = pairs_of(n, L, r0, r1, 0, extent) * flops_per_pair * num_kv_heads;
+            const int64_t share = static_cast<int64_t>(
+                static_cast<double>(prefill_queues) * static_cast<double>(block_flops) /
+                (static_cast<double>(prefill_flops) * num_kv_heads));
+            const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, extent / kPrefillPieceMin));
+            const int64_t ask = std::min<int64_t>(most, std::max<int64_t>(1, share));
             const int64_t piece = ceil_div(ceil_div(extent, ask), kTileTokens) * kTileTokens;
             const int32_t parts = static_cast<int32_t>(ceil_div(extent, piece));  // no empty piece
             const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
@@ -282,7 +284,7 @@ void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int3
     const int64_t merges = seqs + blocks;
     const int64_t prows = nq + seqs + toks * kPrefillMaxPieces;
     const size_t image = align_up(static_cast<size_t>(units) * sizeof(Unit)) +
-                         align_up(static_cast<size_t>(2 * nq + 1) * sizeof(int32_t)) +
+                         align_up(static_cast<size_t>((1 + kPrefillQueuesPerQueue) * nq + 1) * sizeof(int32_t)) +
                          align_up(static_cast<size_t>(merges) * sizeof(Merge));
     const size_t hd = static_cast<size_t>(std::max(num_q_heads, 1)) * static_cast<size_t>(std::max(head_dim, 1));
     const size_t po = align_up(static_cast<size_t>(prows) * hd * sizeof(float));

@@ -139,16 +139,17 @@ def test_mixed_plan_decode_queues_equal_the_decode_plan():
     nq = 96
     p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
     units, qoff, _ = pkv.decode_plan_image(p, image)
-    assert p.num_prefill_queues == nq and len(qoff) == 2 * nq + 1
+    npq = p.num_prefill_queues
+    assert npq == 2 * nq and len(qoff) == nq + npq + 1
     dec = np.nonzero(ql == 1)[0]
     want = split_kv_plan(lens[dec].tolist(), nq)
     got = [[(int(dec.tolist().index(u[0])), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]]
            for q in range(nq)]
     assert got == want
-    pre = units[qoff[nq]:qoff[2 * nq]]
+    pre = units[qoff[nq]:qoff[nq + npq]]
     assert len(pre) == p.num_prefill_units and np.all(pre[:, 7] >= 1)
     assert np.all(units[:qoff[nq], 7] == 0)
-    assert qoff[2 * nq] == p.num_units
+    assert qoff[nq + npq] == p.num_units
 
 
 def test_decode_only_plan_has_no_prefill_queues():
