@@ -254,6 +254,12 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
     // the prefill tile stages 8 elements of a key per load
     const size_t item = 8 * static_cast<size_t>(dt_bytes(kv_dtype));
     if (chunks && (!aligned(k_cache, item) || !aligned(v_cache, item))) return PKV_ERR_SHAPE;
+    if (chunks && mixed_one_launch(q_dtype, kv_dtype, head_dim, group, block_size)) {
+        st = launch_mixed(a, head_dim, group, plan->num_queues, plan->num_prefill_queues, stream);
+        if (st != PKV_OK) return st;
+        const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
+        return launch_merge(a, merges, plan->num_merges, merge_rows(plan, group), q_dtype, head_dim, stream);
+    }
     if (plan->num_units > plan->num_prefill_units) {
         st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
         if (st != PKV_OK) return st;

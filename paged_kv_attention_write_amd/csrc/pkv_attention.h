@@ -56,6 +56,11 @@ int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, in
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 int launch_prefill(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                    int queue0, void* stream);
+// Decode rows and chunks of a mixed step in one launch (bf16 K/V on pages of
+// whole tiles, groups 2 and 4, where one workgroup of each fits a CU).
+bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int block_size);
+int launch_mixed(const AttnArgs& a, int head_dim, int group, int num_decode_queues, int num_prefill_queues,
+                 void* stream);
 // max_rows: the most rows of any merge record (1 for a decode-only plan).
 int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int max_rows, int q_dtype, int head_dim,
                  void* stream);

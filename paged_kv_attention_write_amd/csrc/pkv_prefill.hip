@@ -31,7 +31,7 @@
 // barrier closes the step.
 #include <math.h>
 
-#include "pkv_attention.h"
+#include "pkv_decode_unit.h"
 
 namespace pkv {
 namespace {
@@ -153,12 +153,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 // One tile of one wave: S^T for keys t0 + 16 kb2 + 4 g4 + i of pair n, the
-// online softmax update, and O^T += V^T P^T.
+// online softmax update, and O^T += V^T P^T.  qk = |scale * k_scale * log2 e|
+// (a negative factor is carried by the sign of q, and qk >= 2^-100).  mask
+// (uniform in the wave): the tile crosses the causal diagonal, the end of the
+// key range or rows past the unit, so keys are tested one by one; otherwise
+// every key of the tile is visible to every pair of the wave.  Per score the vector work is one fma into one v_exp_f32,
+// a share of a max3, a packed bf16 conversion and a dot2 into the row sum.
 template <int D, int NS = D / 32, int ND = D / 16>
 __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, int t0, int kend, int pos, bool row_ok,
-                                           int n, int g4, float qk_scale, const bf16x8_t (&qb)[NS],
+                                           bool mask, int n, int g4, float qk, const bf16x8_t (&qb)[NS],
                                            f32x4_t (&acc)[ND], float& m_run, float& l_run) {
-    float sv[8];
+    float sv[8];  // raw q.k
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
@@ -167,16 +172,19 @@ __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, in
             c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_bf16x8(&lds.k[buf][16 * kb2 + n][32 * s + 8 * g4]), qb[s],
                                                         c, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kp = t0 + 16 * kb2 + 4 * g4 + i;
-            sv[4 * kb2 + i] = (row_ok && kp < kend && kp <= pos) ? c[i] * qk_scale : -INFINITY;
+        for (int i = 0; i < 4; ++i) sv[4 * kb2 + i] = c[i];
+    }
+    if (mask) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int kp = t0 + 16 * (j >> 2) + 4 * g4 + (j & 3);
+            sv[j] = (row_ok && kp < kend && kp <= pos) ? sv[j] : -INFINITY;
         }
     }
-    float mt = sv[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float mr = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    mr = fmaxf(mr, __shfl_xor(mr, 16));
+    mr = fmaxf(mr, __shfl_xor(mr, 32));
+    const float mt = (mr == -INFINITY) ? -INFINITY : mr * qk;  // the tile's max in log2 units
     // lazy rescale, as in the decode unit: scores at most 2^8 above the
     // running maximum are taken against it
     const bool need = mt > m_run + 8.0f;
@@ -188,12 +196,19 @@ __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, in
 #pragma unroll
         for (int b = 0; b < ND; ++b) acc[b] *= alpha;
     }
-    const float mb = (m_run == -INFINITY) ? 0.f : m_run;
+    const float nmb = (m_run == -INFINITY) ? 0.f : -m_run;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = exp2_fast(fmaf(sv[j], qk, nmb));  // a masked key (-inf) gives 0
     bf16x8_t pb;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        pb[j] = static_cast<__bf16>(exp2_fast(sv[j] - mb));  // round to nearest even
-        l_run += static_cast<float>(pb[j]);                   // the weights P V uses
+    for (int j = 0; j < 8; ++j) pb[j] = static_cast<__bf16>(p[j]);  // round to nearest even
+    // the row sum adds the rounded weights that P V uses, two per dot2
+    const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bf16x2_t pp = {pb[2 * j], pb[2 * j + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
     }
     // V^T operand: lane group g4 takes keys 4 g4 + j (j < 4) and 16 + 4 g4 +
     // j - 4 (j >= 4), where the first product left their scores; lane 4 j + q
@@ -209,13 +224,12 @@ __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, in
     }
 }
 
+// The prefill units of plan queue `queue` on the calling workgroup.
 template <int KVDT, int D, int G>
-__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-void prefill_kernel(AttnArgs a, int queue0) {
+__device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, PrefillLds<D>& lds) {
     constexpr int QB = 2;       // bf16 queries
     constexpr int NS = D / 32;  // k steps of the first product
     constexpr int ND = D / 16;  // 16-row blocks of O^T
-    __shared__ PrefillLds<D> lds;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -225,8 +239,8 @@ void prefill_kernel(AttnArgs a, int queue0) {
 
     const const_ptr<Unit> units = as_const(a.units);
     const const_ptr<int32_t> qoff = as_const(a.queue_off);
-    const int u_begin = qoff[queue0 + blockIdx.x];
-    const int u_end = qoff[queue0 + blockIdx.x + 1];
+    const int u_begin = qoff[queue];
+    const int u_end = qoff[queue + 1];
     for (int ui = u_begin; ui < u_end; ++ui) {
         const Unit un = load_unit(units, ui);
         const int h = un.kind - kUnitPrefill;
@@ -240,6 +254,9 @@ void prefill_kernel(AttnArgs a, int queue0) {
         const int wr1 = min(un.nrows - 1, (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G);
         const bool wave_has_rows = wr0 < un.nrows;
         const int wave_last_pos = un.pos0 + wr1;
+        const int wave_first_pos = un.pos0 + wr0;
+        // every pair of the wave is a row of the unit
+        const bool wave_full = (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G < un.nrows;
 
         const int n_ctx = as_const(a.context_lens)[un.seq];
         const int kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
@@ -259,9 +276,15 @@ void prefill_kernel(AttnArgs a, int queue0) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) w.w[j] = 0u;
                 }
-                qb[s] = __builtin_bit_cast(bf16x8_t, make_uint4(w.w[0], w.w[1], w.w[2], w.w[3]));
+                // a negative score factor is carried by the sign of q (exact)
+                const uint32_t flip = a.qk_scale < 0.f ? 0x80008000u : 0u;
+                qb[s] = __builtin_bit_cast(bf16x8_t, make_uint4(w.w[0] ^ flip, w.w[1] ^ flip, w.w[2] ^ flip,
+                                                                w.w[3] ^ flip));
             }
         }
+        // |factor|, at least 2^-100 so that -inf * qk stays -inf (a zero
+        // factor then still gives exp2 of exactly 0 for every visible key)
+        const float qk = fmaxf(fabsf(a.qk_scale), 0x1p-100f);
 
         f32x4_t acc[ND];
 #pragma unroll
@@ -291,8 +314,10 @@ void prefill_kernel(AttnArgs a, int queue0) {
         // (loaded two phases ago) into the other buffer and reloads its
         // register set with tile t + 3.
         auto phase = [&](int t0, int buf, PfRegs<KVDT, D>& rs, int32_t& pg) {
-            if (wave_has_rows && t0 <= wave_last_pos)
-                pf_compute<D>(lds, buf, t0, kend, pos, row_ok, n, g4, a.qk_scale, qb, acc, m_run, l_run);
+            if (wave_has_rows && t0 <= wave_last_pos) {
+                const bool mask = !(wave_full && t0 + kPfKeys <= kend && t0 + kPfKeys - 1 <= wave_first_pos);
+                pf_compute<D>(lds, buf, t0, kend, pos, row_ok, mask, n, g4, qk, qb, acc, m_run, l_run);
+            }
             if (t0 + kPfKeys < kend) {
                 pf_stage<KVDT, D>(rs, role, lds, buf ^ 1);
                 const int t3 = t0 + 3 * kPfKeys + role.kk;
@@ -342,6 +367,41 @@ void prefill_kernel(AttnArgs a, int queue0) {
 }
 
 template <int KVDT, int D, int G>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_kernel(AttnArgs a, int queue0) {
+    __shared__ PrefillLds<D> lds;
+    prefill_queue<KVDT, D, G>(a, queue0 + blockIdx.x, lds);
+}
+
+// Both halves of a mixed step in one launch: blocks below num_decode_queues
+// walk the decode queues with the decode unit, the others the prefill queues,
+// so that the bandwidth-bound decode rows and the matrix-core chunk tiles run
+// side by side on every CU (one 8-wave workgroup of each fits at <= 128
+// VGPRs).
+template <int KVDT, int D, int G>
+constexpr size_t mixed_lds_bytes() {
+    return sizeof(DecodeLds<D, G, kPfWaves>) > sizeof(PrefillLds<D>) ? sizeof(DecodeLds<D, G, kPfWaves>)
+                                                                      : sizeof(PrefillLds<D>);
+}
+
+template <int KVDT, int D, int G>
+__global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void mixed_kernel(AttnArgs a, int num_decode_queues) {
+    __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<KVDT, D, G>()];
+    const int b = blockIdx.x;
+    if (b < num_decode_queues) {
+        const const_ptr<Unit> units = as_const(a.units);
+        const const_ptr<int32_t> qoff = as_const(a.queue_off);
+        const int u_end = qoff[b + 1];
+        for (int ui = qoff[b]; ui < u_end; ++ui)
+            decode_unit<PKV_DTYPE_BF16, KVDT, D, G, kPfWaves, true>(
+                a, load_unit(units, ui), *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(smem));
+    } else {
+        prefill_queue<KVDT, D, G>(a, b, *reinterpret_cast<PrefillLds<D>*>(smem));
+    }
+}
+
+template <int KVDT, int D, int G>
 int launch_prefill_t(const AttnArgs& a, int num_queues, int queue0, hipStream_t st) {
     hipLaunchKernelGGL((prefill_kernel<KVDT, D, G>), dim3(num_queues), dim3(kPfWaves * 64), 0, st, a, queue0);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -365,7 +425,35 @@ int launch_prefill_d(const AttnArgs& a, int d, int group, int num_queues, int qu
     return PKV_ERR_UNSUPPORTED;
 }
 
+template <int KVDT>
+int launch_mixed_d(const AttnArgs& a, int d, int group, int num_decode_queues, int num_prefill_queues,
+                   hipStream_t st) {
+    const dim3 grid(num_decode_queues + num_prefill_queues), block(kPfWaves * 64);
+    if (d == 128 && group == 4)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4>), grid, block, 0, st, a, num_decode_queues);
+    else if (d == 128 && group == 2)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2>), grid, block, 0, st, a, num_decode_queues);
+    else if (d == 64 && group == 4)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 4>), grid, block, 0, st, a, num_decode_queues);
+    else if (d == 64 && group == 2)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 2>), grid, block, 0, st, a, num_decode_queues);
+    else
+        return PKV_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace
+
+bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int block_size) {
+    return q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_BF16 && (head_dim == 64 || head_dim == 128) &&
+           (group == 2 || group == 4) && block_size % kTileTokens == 0;
+}
+
+int launch_mixed(const AttnArgs& a, int head_dim, int group, int num_decode_queues, int num_prefill_queues,
+                 void* stream) {
+    return launch_mixed_d<PKV_DTYPE_BF16>(a, head_dim, group, num_decode_queues, num_prefill_queues,
+                                          static_cast<hipStream_t>(stream));
+}
 
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
     return q_dtype == PKV_DTYPE_BF16 && (kv_dtype == PKV_DTYPE_BF16 || kv_dtype == PKV_DTYPE_FP8_E4M3) &&

@@ -80,6 +80,18 @@ def test_mixed_fp8_cache(gpu, d):
     check_close(out, ref, "fp8", f"mixed fp8 d={d}")
 
 
+@pytest.mark.parametrize("scale", [-0.07, 0.0, 0.3])
+def test_mixed_scale_sign_and_zero(gpu, scale):
+    """A negative score factor (carried by the sign of q in the chunk tile), a
+    zero factor (uniform weights over the visible keys) and a large one."""
+    lens = [300, 40, 520]
+    ql = [100, 1, 37]
+    case = workloads.build_case("mxs", 96, lens, ql, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                                scale=scale)
+    out, ref, _ = _run(case, gpu, 5)
+    check_close(out, ref, "bf16", f"mixed scale={scale}")
+
+
 def test_mixed_packing_order(gpu):
     """The chunk first or last in [T]: each sequence's rows match the oracle either way."""
     for order in ("chunk-last", "chunk-first"):
