@@ -286,11 +286,12 @@ def main():
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
     plan_s = []
+    wait_s = []
 
     def step(timed_index=None):
-        t0 = time.perf_counter()
         plan.update(st["context_lens"], q_lens)
-        plan_s.append(time.perf_counter() - t0)
+        plan_s.append(plan.last_plan_s)
+        wait_s.append(plan.last_wait_s)
         for l, layer in enumerate(layers):
             ks, vs = scales[l]
             pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
@@ -310,6 +311,7 @@ def main():
         step()
     torch.cuda.synchronize()
     plan_s.clear()
+    wait_s.clear()
     log("timed")
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -366,6 +368,7 @@ def main():
                               "p90": round(float(np.percentile(decode_ms, 90)) * 1e3, 3)},
         "plan_us_per_step": round(float(np.median(plan_s)) * 1e6, 2),
         "plan_us_per_layer": round(float(np.median(plan_s)) * 1e6 / args.layers, 3),
+        "plan_staging_wait_us_per_step": round(float(np.median(wait_s)) * 1e6, 2),
         "roofline": roofline,
         "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
                  "merges": int(plan.desc.num_merges), "target_tiles": int(plan.desc.target_tiles)},

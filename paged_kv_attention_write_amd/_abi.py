@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import time
 from typing import Optional
 
 import numpy as np
@@ -231,6 +232,9 @@ class Plan:
     for new lengths into the same buffers when they are large enough.  The
     upload is ordered on the stream like any kernel, so a re-plan issued
     after the previous step's attention calls on the same stream is safe.
+    ``last_plan_s`` is the host time of the last planner call (plan and
+    upload issue) and ``last_wait_s`` the time spent waiting for a staging
+    buffer to come free before it.
     """
 
     def __init__(self, context_lens, q_lens=None, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -254,18 +258,22 @@ class Plan:
         ql_ptr = None if ql is None else ql.ctypes.data
         i = self._turn
         self._turn ^= 1
+        t0 = time.perf_counter()
         if self._uploaded[i] is not None:
             self._uploaded[i].synchronize()  # this staging buffer's last upload (two updates ago) has run
+        self.last_wait_s = time.perf_counter() - t0
         with torch.cuda.device(self.device):
             st_ptr = _stream(stream, self.device)
             for attempt in range(2):
                 staging, ws = self._staging[i], self.workspace
+                t1 = time.perf_counter()
                 st = lib().paged_attn_plan(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads, self.num_kv_heads,
                                            self.head_dim, self.num_queues,
                                            staging.data_ptr() if staging is not None else None,
                                            staging.numel() if staging is not None else 0,
                                            ws.data_ptr() if ws is not None else None,
                                            ws.numel() if ws is not None else 0, ctypes.byref(self.desc), st_ptr)
+                self.last_plan_s = time.perf_counter() - t1
                 if st in (PKV_ERR_WORKSPACE, PKV_ERR_NULL) and attempt == 0:
                     probe = PkvPlan()
                     _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,

@@ -108,30 +108,36 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
     }
 }
 
-// Launch shape: one persistent workgroup per queue, at <= 128 VGPRs per lane
-// where possible (four waves per SIMD).  8 waves (one per kv head of the
-// 8-head workloads) stream bf16 / fp32 K/V on whole-tile pages; 16 waves
-// (two per kv head, alternate tiles) hide the extra latency of per-token page
-// lookups and the fp8 conversion work.  Group 8 (eight q heads per lane),
-// group 1 (sixteen tokens in flight per lane) and fp32 K/V need more
-// registers and keep 8 waves at two waves per SIMD.
+// Launch shape: one persistent workgroup per queue.  8 waves (one per kv head
+// of the 8-head workloads) stream bf16 / fp32 K/V on whole-tile pages (one
+// workgroup per CU: more loads in flight per CU lower the read rate of this
+// pattern).  16 waves (two per kv head, alternate tiles, <= 128 VGPRs) hide
+// the extra latency of per-token page lookups and the fp8 conversion work.
+// Group 8 (eight q heads per lane), group 1 (sixteen tokens in flight per
+// lane) and fp32 K/V need more registers and keep 8 waves at two waves per
+// SIMD.
 template <int QDT, int KVDT, int D, int G>
 int launch_decode_t(const AttnArgs& a, int num_queues, bool uniform, hipStream_t st) {
-    constexpr int WPE = (G == 8 || G == 1 || KVDT == PKV_DTYPE_F32) ? 2 : 4;
-    constexpr bool kCanWiden = WPE == 4;
-    const bool wide = kCanWiden && (!uniform || KVDT == PKV_DTYPE_FP8_E4M3);
-    if (wide) {
-        constexpr int NW = kCanWiden ? 16 : 8;
-        if (uniform)
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, NW, true, WPE>), dim3(num_queues), dim3(NW * 64), 0,
-                               st, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, NW, false, WPE>), dim3(num_queues), dim3(NW * 64), 0,
-                               st, a);
-    } else if (uniform) {
-        hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, WPE>), dim3(num_queues), dim3(8 * 64), 0, st, a);
+    constexpr bool kSmallRegs = !(G == 8 || G == 1 || KVDT == PKV_DTYPE_F32);
+    const dim3 grid(num_queues);
+    if constexpr (kSmallRegs) {
+        if constexpr (KVDT == PKV_DTYPE_FP8_E4M3) {
+            if (uniform)
+                hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, true, 4>), grid, dim3(16 * 64), 0, st,
+                                   a);
+            else
+                hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, false, 4>), grid, dim3(16 * 64), 0, st,
+                                   a);
+        } else if (uniform) {
+            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, 4>), grid, dim3(8 * 64), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, false, 4>), grid, dim3(16 * 64), 0, st, a);
+        }
     } else {
-        hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, false, WPE>), dim3(num_queues), dim3(8 * 64), 0, st, a);
+        if (uniform)
+            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, 2>), grid, dim3(8 * 64), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, false, 2>), grid, dim3(8 * 64), 0, st, a);
     }
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

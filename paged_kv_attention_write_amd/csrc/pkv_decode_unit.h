@@ -94,14 +94,18 @@ __device__ __forceinline__ void kv_to_f32(float (&x)[EPL], const Words<KW>& r) {
 // row `row`).  With pages of a multiple of 16 tokens the page of every
 // 16-token sub-tile is one scalar load and the group's base address is
 // scalar; the per-lane part is a 32-bit byte offset.  FULL: every token of
-// the tile is below ke.  Loads are never skipped: a token outside the piece
-// (or on a page outside the pool) reads the first bytes of the pool instead,
-// and its V is zeroed (its score is masked to -inf by the caller).
+// the tile is below ke.  Every load is issued, unconditionally, so that the
+// wait before the products can count exactly the loads still in flight: a
+// lane whose token is past the piece reads the unit's clamp token instead
+// (`clamp_off`: the last key of the piece).  The caller masks the scores of
+// those lanes to -inf, so their p is exactly 0 and the (finite) clamp values
+// add nothing.  A token on a page outside the pool sets `bad` (its rows are
+// written as NaN) and reads the pool start or the clamp token.
 template <int KVDT, int D, int U, int KW, bool UNIFORM_PAGE, bool FULL>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
                                           const_ptr<int32_t> tbl, const char* kc, const char* vc, int t0, int ke,
                                           int row, uint32_t lane_off, uint32_t head_off, int64_t tok_bytes,
-                                          bool& bad) {
+                                          int64_t clamp_off, bool& bad) {
     const int bs = a.block_size;
     // block ids are int32: a pool of more than 2^31 - 1 blocks is addressed up to that many
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
@@ -126,39 +130,51 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
             for (int uu = 0; uu < PER; ++uu) {
                 const int u = 4 * s + uu;
                 if constexpr (FULL) {
+                    // a page outside the pool reads the pool start: its rows come out NaN anyway
                     k[u] = load_words_nt<KW>(kb + 4 * uu * tok_bytes + lane_off);
                     v[u] = load_words_nt<KW>(vb + 4 * uu * tok_bytes + lane_off);
                 } else {
                     const bool ok = pok && t0 + 4 * u + row < ke;
-                    const int64_t off = ok ? 4 * uu * tok_bytes + lane_off : 0;
-                    k[u] = load_words<KW>(kb + off);
-                    Words<KW> vv = load_words<KW>(vb + off);
-#pragma unroll
-                    for (int w = 0; w < KW; ++w) vv.w[w] = ok ? vv.w[w] : 0u;
-                    v[u] = vv;
+                    const int64_t off = ok ? slot0 * tok_bytes + 4 * uu * tok_bytes + lane_off : clamp_off;
+                    k[u] = load_words_nt<KW>(kc + off);
+                    v[u] = load_words_nt<KW>(vc + off);
                 }
             }
         }
     } else {
-        // one lookup per token: lane row r reads the page of token t0 + 4u + r
+        // one lookup per token: lane row r reads the page of token t0 + 4u + r;
+        // the table is read at a clamped index, unconditionally
+        const int last_pidx = (ke - 1) / bs;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = t0 + 4 * u + row;
             const bool tv = FULL || t < ke;
-            const int pidx = t / bs;
-            const uint32_t page = static_cast<uint32_t>((tv && pidx < a.max_blocks) ? tbl[pidx] : -1);
-            const bool ok = tv && page < nblocks;  // a negative id wraps to >= 2^31
+            const int pidx = tv ? t / bs : last_pidx;
+            const uint32_t page = static_cast<uint32_t>(tbl[min(pidx, a.max_blocks - 1)]);
+            const bool ok = tv && pidx < a.max_blocks && page < nblocks;  // a negative id wraps to >= 2^31
             bad |= tv && !ok;
             const uint64_t slot = static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
                                   static_cast<uint32_t>(t - pidx * bs);
-            const int64_t off = ok ? static_cast<int64_t>(slot) * tok_bytes + head_off : 0;
+            const int64_t off = ok ? static_cast<int64_t>(slot) * tok_bytes + head_off : clamp_off;
             k[u] = load_words<KW>(kc + off);
-            Words<KW> vv = load_words<KW>(vc + off);
-#pragma unroll
-            for (int w = 0; w < KW; ++w) vv.w[w] = ok ? vv.w[w] : 0u;
-            v[u] = vv;
+            v[u] = load_words<KW>(vc + off);
         }
     }
+}
+
+// Byte offset (inside a pool) of the clamp token of a piece ending at ke:
+// key ke - 1 of the sequence, at the lane's head offset, or the head offset
+// alone when that key's page is outside the pool.
+__device__ __forceinline__ int64_t clamp_offset(const AttnArgs& a, const_ptr<int32_t> tbl, int ke,
+                                                uint32_t head_off, int64_t tok_bytes) {
+    const int bs = a.block_size;
+    const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
+    const int t = ke - 1;
+    const int pidx = t / bs;
+    const uint32_t page = static_cast<uint32_t>(pidx < a.max_blocks ? tbl[pidx] : -1);
+    if (page >= nblocks) return head_off;
+    return static_cast<int64_t>(static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
+                                static_cast<uint32_t>(t - pidx * bs)) * tok_bytes + head_off;
 }
 
 // Scores in log2 units above the running maximum by at most this much are
@@ -280,6 +296,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         for (int g = 0; g < G; ++g) load_q<QDT, KVDT, D>(q[g], qbase + static_cast<int64_t>(g) * D * QB);
         const uint32_t head_off = static_cast<uint32_t>((h * D + col * EPL) * KVB);  // inside a token
         const uint32_t lane_off = row * row_bytes + head_off;
+        const int64_t clamp_off = kb < ke ? clamp_offset(a, tbl, ke, head_off, tok_bytes) : head_off;
 
         float acc[G][EPL];
 #pragma unroll
@@ -291,15 +308,18 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         bool bad = false;
 
         const int step = TT * tp;
-        for (int t0 = kb + sub * TT; t0 < ke; t0 += step) {
-            Words<KW> kr[U], vr[U];
+        auto load_any = [&](Words<KW>(&kr)[U], Words<KW>(&vr)[U], int t0) {
             if (t0 + TT <= ke) {
                 load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, kc, vc, t0, ke, row, lane_off,
-                                                              head_off, tok_bytes, bad);
+                                                              head_off, tok_bytes, clamp_off, bad);
             } else {
                 load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, kc, vc, t0, ke, row, lane_off,
-                                                               head_off, tok_bytes, bad);
+                                                               head_off, tok_bytes, clamp_off, bad);
             }
+        };
+        for (int t0 = kb + sub * TT; t0 < ke; t0 += step) {
+            Words<KW> kr[U], vr[U];
+            load_any(kr, vr, t0);
             process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale,
                                                       t0 + my_tok < ke, col);
         }
