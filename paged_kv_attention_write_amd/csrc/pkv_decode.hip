@@ -23,11 +23,13 @@ void decode_kernel(AttnArgs a) {
 }
 
 // Merge of the partial results of cut sequences.  One wave per (merge record,
-// row, head): lane c reads part c's lse (log2 units), a wave max and sum give
-// the part weights w_c = 2^(lse_c - M) / sum, then every lane accumulates its
-// D/64 elements over the parts with independent loads.  Grid: (merge record,
-// row of the record, group of kMergeWaves heads).
+// row, head): the parts' lse values (log2 units, wave-uniform: scalar loads)
+// and each lane's D/64 elements of every part are loaded together, up to
+// kMergeBatch parts at a time, so a record of up to that many parts costs one
+// round trip to memory; batches combine by an online log-sum-exp.  Grid:
+// (merge record, row of the record, group of kMergeWaves heads).
 constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 8;
 
 template <int QDT, int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __restrict__ merges,
@@ -35,76 +37,64 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
                                                                  const float* __restrict__ pl,
                                                                  void* __restrict__ out, int hq, float v_scale) {
     constexpr int E = D / 64;  // elements per lane
-    const Merge mg = merges[blockIdx.x];
+    constexpr int B = kMergeBatch;
+    const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + blockIdx.x);
+    const int row0 = mw[0], nrows = mw[1], prow0 = mw[2], parts = mw[3];
     const int r = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int h = blockIdx.z * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (h >= hq || r >= mg.nrows) return;
+    if (h >= hq || r >= nrows) return;
     const int64_t hd = static_cast<int64_t>(hq) * D;
-    {
-        // weights of the parts, 64 at a time
-        float M = -INFINITY;
-        bool nan = false;
-        for (int c0 = 0; c0 < mg.parts; c0 += 64) {
-            const int c = c0 + lane;
-            const float x = c < mg.parts ? pl[static_cast<int64_t>(mg.prow0 + c * mg.nrows + r) * hq + h] : -INFINITY;
-            nan |= (x != x);
-            M = fmaxf(M, x);
+    const const_ptr<float> lse = as_const(pl);
+    float M = -INFINITY;  // running maximum of the lse values seen
+    float sw = 0.f;       // sum of 2^(lse - M)
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    bool nan = false;
+    for (int c0 = 0; c0 < parts; c0 += B) {
+        float l[B];
+        float x[B][E];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int64_t prow = prow0 + static_cast<int64_t>(min(c0 + b, parts - 1)) * nrows + r;
+            l[b] = lse[prow * hq + h];
+            const float* src = po + prow * hd + static_cast<int64_t>(h) * D + lane * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[b][e] = src[e];
         }
-        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        nan = __any(nan);
-        float acc[E];
+        float mb = M;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = 0.f;
-        float sw = 0.f;
-        if (!nan && M != -INFINITY) {
-            for (int c0 = 0; c0 < mg.parts; c0 += 64) {
-                const int c = c0 + lane;
-                const float w = c < mg.parts
-                                    ? exp2_fast(pl[static_cast<int64_t>(mg.prow0 + c * mg.nrows + r) * hq + h] - M)
-                                    : 0.f;
-                float ws = w;
-                for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o);
-                sw += ws;
-                const int n = min(64, mg.parts - c0);
-                int j = 0;
-                for (; j + 4 <= n; j += 4) {
-                    float v[4][E];
-                    float wj[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        wj[k] = __shfl(w, j + k);
-                        const float* src = po + static_cast<int64_t>(mg.prow0 + (c0 + j + k) * mg.nrows + r) * hd +
-                                           static_cast<int64_t>(h) * D + lane * E;
-#pragma unroll
-                        for (int e = 0; e < E; ++e) v[k][e] = src[e];
-                    }
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-#pragma unroll
-                        for (int e = 0; e < E; ++e) acc[e] = fmaf(wj[k], v[k][e], acc[e]);
-                }
-                for (; j < n; ++j) {
-                    const float wj = __shfl(w, j);
-                    const float* src = po + static_cast<int64_t>(mg.prow0 + (c0 + j) * mg.nrows + r) * hd +
-                                       static_cast<int64_t>(h) * D + lane * E;
-#pragma unroll
-                    for (int e = 0; e < E; ++e) acc[e] = fmaf(wj, src[e], acc[e]);
-                }
-            }
+        for (int b = 0; b < B; ++b) {
+            if (c0 + b >= parts) l[b] = -INFINITY;  // a repeated last part counts once
+            nan |= l[b] != l[b];
+            mb = fmaxf(mb, l[b]);
         }
-        float o[E];
-        const float scale = (sw > 0.f) ? v_scale / sw : 0.f;
+        if (mb == -INFINITY) continue;  // every part so far is empty
+        const float f = exp2_fast(M - mb);  // 0 while M is -inf
+        sw *= f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = nan ? NAN : acc[e] * scale;
-        const int64_t oi = static_cast<int64_t>(mg.row0 + r) * hd + static_cast<int64_t>(h) * D + lane * E;
-        if constexpr (QDT == PKV_DTYPE_F32) {
+        for (int e = 0; e < E; ++e) acc[e] *= f;
 #pragma unroll
-            for (int e = 0; e < E; ++e) static_cast<float*>(out)[oi + e] = o[e];
-        } else {
+        for (int b = 0; b < B; ++b) {
+            const float w = exp2_fast(l[b] - mb);  // 0 for an empty part
+            sw += w;
 #pragma unroll
-            for (int e = 0; e < E; ++e) static_cast<uint16_t*>(out)[oi + e] = static_cast<uint16_t>(f32_to_bf16_rne(o[e]));
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[b][e], acc[e]);
         }
+        M = mb;
+    }
+    const float scale = sw > 0.f ? v_scale / sw : 0.f;
+    float o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = nan ? NAN : acc[e] * scale;
+    const int64_t oi = static_cast<int64_t>(row0 + r) * hd + static_cast<int64_t>(h) * D + lane * E;
+    if constexpr (QDT == PKV_DTYPE_F32) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) static_cast<float*>(out)[oi + e] = o[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) static_cast<uint16_t*>(out)[oi + e] = static_cast<uint16_t>(f32_to_bf16_rne(o[e]));
     }
 }
 

@@ -93,7 +93,8 @@ __device__ __forceinline__ void kv_to_f32(float (&x)[EPL], const Words<KW>& r) {
 // Loads of one wave-tile: U groups of 4 tokens (token t0 + 4u + row in lane
 // row `row`).  With pages of a multiple of 16 tokens the page of every
 // 16-token sub-tile is one scalar load and the group's base address is
-// scalar; the per-lane part is a 32-bit byte offset.  FULL: every token of
+// scalar (from `pages`, looked up by the caller); the per-lane part is a
+// 32-bit byte offset.  FULL: every token of
 // the tile is below ke.  Every load is issued, unconditionally, so that the
 // wait before the products can count exactly the loads still in flight: a
 // lane whose token is past the piece reads the unit's clamp token instead
@@ -101,23 +102,41 @@ __device__ __forceinline__ void kv_to_f32(float (&x)[EPL], const Words<KW>& r) {
 // those lanes to -inf, so their p is exactly 0 and the (finite) clamp values
 // add nothing.  A token on a page outside the pool sets `bad` (its rows are
 // written as NaN) and reads the pool start or the clamp token.
+// Sub-tiles of 16 tokens in a wave-tile of U groups of 4 tokens (pages of a
+// multiple of 16 tokens: one page id per sub-tile).
+template <int U>
+constexpr int kSubTiles = U >= 4 ? U / 4 : 1;
+
+// Page ids of the sub-tiles of the wave-tile at t0 (-1 past ke or past the
+// table): scalar loads, issued a tile ahead of their use.
+template <int U>
+__device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const AttnArgs& a,
+                                           const_ptr<int32_t> tbl, int t0, int ke) {
+#pragma unroll
+    for (int s = 0; s < kSubTiles<U>; ++s) {
+        const int ts = t0 + 16 * s;
+        const int pidx = ts / a.block_size;
+        pages[s] = (ts < ke && pidx < a.max_blocks) ? tbl[pidx] : -1;
+    }
+}
+
 template <int KVDT, int D, int U, int KW, bool UNIFORM_PAGE, bool FULL>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
-                                          const_ptr<int32_t> tbl, const char* kc, const char* vc, int t0, int ke,
-                                          int row, uint32_t lane_off, uint32_t head_off, int64_t tok_bytes,
-                                          int64_t clamp_off, bool& bad) {
+                                          const_ptr<int32_t> tbl, const int32_t (&pages)[kSubTiles<U>],
+                                          const char* kc, const char* vc, int t0, int ke, int row, uint32_t lane_off,
+                                          uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, bool& bad) {
     const int bs = a.block_size;
     // block ids are int32: a pool of more than 2^31 - 1 blocks is addressed up to that many
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     if constexpr (UNIFORM_PAGE) {
-        constexpr int SUB = U >= 4 ? U / 4 : 1;
+        constexpr int SUB = kSubTiles<U>;
         constexpr int PER = U < 4 ? U : 4;
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             const int ts = t0 + 16 * s;
             const int pidx = ts / bs;
             const bool in = FULL || ts < ke;
-            const uint32_t page = static_cast<uint32_t>((in && pidx < a.max_blocks) ? tbl[pidx] : -1);
+            const uint32_t page = static_cast<uint32_t>(pages[s]);
             const bool pok = page < nblocks;  // a negative id wraps to >= 2^31
             if (in && !pok) bad = true;
             const int64_t slot0 =
@@ -308,18 +327,21 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         bool bad = false;
 
         const int step = TT * tp;
-        auto load_any = [&](Words<KW>(&kr)[U], Words<KW>(&vr)[U], int t0) {
-            if (t0 + TT <= ke) {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, kc, vc, t0, ke, row, lane_off,
-                                                              head_off, tok_bytes, clamp_off, bad);
-            } else {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, kc, vc, t0, ke, row, lane_off,
-                                                               head_off, tok_bytes, clamp_off, bad);
-            }
-        };
+        // Whole-tile pages: the page ids of the wave's next tile are loaded
+        // while this tile is computed, so the next tile's K/V loads need not
+        // wait for a table read.
+        int32_t pages[kSubTiles<U>];
+        if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, kb + sub * TT, ke);
         for (int t0 = kb + sub * TT; t0 < ke; t0 += step) {
             Words<KW> kr[U], vr[U];
-            load_any(kr, vr, t0);
+            if (t0 + TT <= ke) {
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, pages, kc, vc, t0, ke, row, lane_off,
+                                                              head_off, tok_bytes, clamp_off, bad);
+            } else {
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, pages, kc, vc, t0, ke, row,
+                                                               lane_off, head_off, tok_bytes, clamp_off, bad);
+            }
+            if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, t0 + step, ke);
             process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale,
                                                       t0 + my_tok < ke, col);
         }
