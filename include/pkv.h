@@ -52,7 +52,9 @@
  *     sits at position n - L + i and sees keys 0 .. n - L + i.
  *   - Device-side contents are trusted except where stated: a block id
  *     outside [0, num_blocks) is never dereferenced; the rows of a sequence
- *     whose table holds one come out as NaN.
+ *     whose table holds one come out as NaN.  Decode rows take their key
+ *     ranges from the plan; a decode row whose context_lens entry differs
+ *     from the length the plan was made from (a stale plan) comes out as NaN.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef PKV_H_

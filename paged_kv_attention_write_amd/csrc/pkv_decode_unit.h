@@ -301,7 +301,12 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
     const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
     const const_ptr<int32_t> ctx = as_const(a.context_lens);
 
-    const int n = ctx[un.seq];
+    // The key range comes from the plan alone (a decode row sits at position
+    // n - 1), so the first loads need not wait for a length read; the
+    // device length is read alongside and checked at the end: a sequence
+    // whose length differs from the plan's (a stale plan) gets NaN rows.
+    const int n = un.pos0 + 1;
+    const int n_dev = ctx[un.seq];
     const int kb = un.kv_begin;
     const int ke = min(un.kv_end, n);
     const const_ptr<int32_t> tbl = as_const(a.block_tables) + static_cast<int64_t>(un.seq) * a.max_blocks;
@@ -354,7 +359,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         });
 
         // merge the four rows of the wave
-        bad = __any(bad);
+        bad = __any(bad) || n_dev != n;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float M = rows4_max(m[g]);

@@ -29,7 +29,7 @@ constexpr int kDppRowNewBcast = 0x150;    // + n: every lane of the row <- lane 
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sum over the 16 lanes of each row; every lane of the row gets the total.

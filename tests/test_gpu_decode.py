@@ -125,6 +125,30 @@ def test_invalid_block_id_gives_nan_rows_only_for_that_sequence(gpu):
     check_close(out[[0, 2]], ref[[0, 2]], "bf16", "neighbours of the bad sequence")
 
 
+@pytest.mark.parametrize("changed", [0, 1])
+def test_stale_plan_length_gives_nan_rows(gpu, changed):
+    """Decode rows take their key ranges from the plan; a device length that
+    differs from the length the plan was made from turns that row into NaN
+    (sequence 0 is one piece, sequence 1 is cut over several queues) and
+    leaves the other rows unaffected."""
+    log(f"stale plan, sequence {changed}")
+    case = workloads.build_case("stale", 62, [50, 900, 33], [1, 1, 1], num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, block_size=16)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    plan = dc.plan(5)  # from the case's own lengths
+    assert plan.desc.num_merges == 1
+    ctx = case.context_lens.copy()
+    ctx[changed] -= 1
+    dc.ctx = to_dev(ctx, gpu)
+    out = as_f64(dc.decode(plan))
+    assert np.all(np.isnan(out[changed]))
+    others = [s for s in range(3) if s != changed]
+    check_close(out[others], ref[others], "bf16", "rows of the unchanged sequences")
+
+
 @pytest.mark.parametrize("layout", ["page1", "page16", "contig"])
 def test_long_context_layouts_sampled(gpu, layout):
     """16 x 32768 at page 1 (shuffled), page 16 (shuffled) or a contiguous slab;
