@@ -162,7 +162,7 @@ COPY_BYTES = 1 << 30
 # Sources that define the kernels of one paged_attn_decode call (decode and
 # merge kernels, the plan they walk).  A traffic record taken from the byte
 # counters is reported only while these sources are unchanged.
-DECODE_SOURCES = ["pkv_decode.hip", "pkv_device.h", "pkv_attention.h", "pkv_internal.h", "pkv_plan.cpp"]
+DECODE_SOURCES = ["pkv_decode.hip", "pkv_decode_unit.h", "pkv_device.h", "pkv_attention.h", "pkv_internal.h", "pkv_plan.cpp"]
 
 
 def decode_source_digest():

@@ -271,86 +271,134 @@ struct DecodeLds {
     int bad[NW];
 };
 
-// One decode unit on the calling workgroup (every wave calls it with the same
-// unit).  Contains __syncthreads when waves share a kv head.
+// One run of decode work on the calling workgroup: one unit's query row
+// against a range of its keys, for the kv head(s) of each wave.  `open` sets
+// up a unit for kv head h of this wave (q slice, empty softmax state),
+// `tiles` accumulates keys [ta, tb) of the unit (ta a multiple of 16 past
+// kv_begin), `flush` combines the wave's four rows and the waves sharing the
+// head and writes the result: the output row (`direct`) or a normalised
+// partial with its log-sum-exp at partial row `prow`.  Every wave of the
+// workgroup makes the same calls (flush contains barriers when waves share a
+// head).
 template <int QDT, int KVDT, int D, int G, int NW, bool UNIFORM_PAGE>
-__device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, DecodeLds<D, G, NW>& lds) {
+struct DecodeRun {
     using R = DecodeRegs<QDT, KVDT, D, G>;
-    constexpr int EPL = R::EPL;
-    constexpr int KW = R::KW;
-    constexpr int QB = dt_bytes(QDT);
-    constexpr int KVB = dt_bytes(KVDT);
-    constexpr int U = 16 / G;  // tokens per lane per wave-tile
-    constexpr int TT = 4 * U;  // tokens per wave-tile
+    static constexpr int EPL = R::EPL;
+    static constexpr int KW = R::KW;
+    static constexpr int QB = dt_bytes(QDT);
+    static constexpr int KVB = dt_bytes(KVDT);
+    static constexpr int U = 16 / G;  // tokens per lane per wave-tile
+    static constexpr int TT = 4 * U;  // tokens per wave-tile
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row = lane >> 4;
-    const int col = lane & 15;
-    const int my_tok = 4 * (col / G) + row;  // token offset in the tile of this lane's score
-    const int hkv = a.hkv;
-    const int tp = (hkv <= NW && NW % hkv == 0) ? NW / hkv : 1;  // waves per kv head
-    const int sub = wave % tp;
-    const int head0 = wave / tp;
-    const int hstep = NW / tp;
-    const int64_t hq_d = static_cast<int64_t>(a.hq) * D;
-    const int64_t tok_bytes = static_cast<int64_t>(hkv) * D * KVB;  // one token, all kv heads
-    const uint32_t row_bytes = static_cast<uint32_t>(tok_bytes);
+    // lane geometry
+    int lane, wave, row, col, my_tok;
+    int tp, sub, head0, hstep;  // waves per kv head, this wave's place among them, first head, head stride
+    int64_t tok_bytes;
+    // the unit
+    Unit un;
+    int n, n_dev, kb, ke, h;
+    const_ptr<int32_t> tbl;
+    uint32_t head_off, lane_off;
+    int64_t clamp_off;
+    // softmax state of this wave's head
+    QSlice<QDT, KVDT, D> q[G];
+    float acc[G][EPL];
+    float m_run, l_run;
+    bool bad;
+    // page ids of the wave-tile at token pf_t of the open unit, loaded ahead
+    // (pf_t < 0: none)
+    int32_t pf_pages[kSubTiles<U>];
+    int pf_t;
 
-    const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
-    const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
-    const const_ptr<int32_t> ctx = as_const(a.context_lens);
+    __device__ __forceinline__ explicit DecodeRun(const AttnArgs& a) {
+        lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        row = lane >> 4;
+        col = lane & 15;
+        my_tok = 4 * (col / G) + row;  // token offset in the tile of this lane's score
+        const int hkv = a.hkv;
+        tp = (hkv <= NW && NW % hkv == 0) ? NW / hkv : 1;
+        sub = wave % tp;
+        head0 = wave / tp;
+        hstep = NW / tp;
+        tok_bytes = static_cast<int64_t>(hkv) * D * KVB;  // one token, all kv heads
+    }
 
     // The key range comes from the plan alone (a decode row sits at position
     // n - 1), so the first loads need not wait for a length read; the
-    // device length is read alongside and checked at the end: a sequence
+    // device length is read alongside and checked at the flush: a sequence
     // whose length differs from the plan's (a stale plan) gets NaN rows.
-    const int n = un.pos0 + 1;
-    const int n_dev = ctx[un.seq];
-    const int kb = un.kv_begin;
-    const int ke = min(un.kv_end, n);
-    const const_ptr<int32_t> tbl = as_const(a.block_tables) + static_cast<int64_t>(un.seq) * a.max_blocks;
-
-    for (int h = head0; h < hkv; h += hstep) {
-        QSlice<QDT, KVDT, D> q[G];
+    __device__ __forceinline__ void open(const AttnArgs& a, const Unit& u, int head) {
+        un = u;
+        h = head;
+        n = u.pos0 + 1;
+        n_dev = as_const(a.context_lens)[u.seq];
+        kb = u.kv_begin;
+        ke = min(u.kv_end, n);
+        tbl = as_const(a.block_tables) + static_cast<int64_t>(u.seq) * a.max_blocks;
         const char* qbase = static_cast<const char*>(a.q) +
-                            (static_cast<int64_t>(un.row0) * a.q_stride + static_cast<int64_t>(h) * G * D +
+                            (static_cast<int64_t>(u.row0) * a.q_stride + static_cast<int64_t>(h) * G * D +
                              col * EPL) * QB;
 #pragma unroll
         for (int g = 0; g < G; ++g) load_q<QDT, KVDT, D>(q[g], qbase + static_cast<int64_t>(g) * D * QB);
-        const uint32_t head_off = static_cast<uint32_t>((h * D + col * EPL) * KVB);  // inside a token
-        const uint32_t lane_off = row * row_bytes + head_off;
-        const int64_t clamp_off = kb < ke ? clamp_offset(a, tbl, ke, head_off, tok_bytes) : head_off;
-
-        float acc[G][EPL];
+        head_off = static_cast<uint32_t>((h * D + col * EPL) * KVB);  // inside a token
+        lane_off = row * static_cast<uint32_t>(tok_bytes) + head_off;
+        clamp_off = kb < ke ? clamp_offset(a, tbl, ke, head_off, tok_bytes) : head_off;
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-        float m_run = -INFINITY;  // running max of this lane's head (the head's lanes agree)
-        float l_run = 0.f;        // running sum of 2^(s - m_run) of this lane's head
-        bool bad = false;
+        m_run = -INFINITY;  // running max of this lane's head (the head's lanes agree)
+        l_run = 0.f;        // running sum of 2^(s - m_run) of this lane's head
+        bad = false;
+        pf_t = -1;
+    }
 
+    // Keys [ta, tb) of the open unit (tb <= ke).  Tokens past tb are masked:
+    // they may belong to another workgroup's range.  `next` (a multiple of
+    // 16 past kv_begin, or -1) is where the caller expects its next range of
+    // this unit to start: the page ids of that wave-tile are loaded during
+    // the last tile of this range.
+    __device__ __forceinline__ void tiles(const AttnArgs& a, int ta, int tb, int next = -1) {
+        const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
+        const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
         const int step = TT * tp;
         // Whole-tile pages: the page ids of the wave's next tile are loaded
         // while this tile is computed, so the next tile's K/V loads need not
         // wait for a table read.
         int32_t pages[kSubTiles<U>];
-        if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, kb + sub * TT, ke);
-        for (int t0 = kb + sub * TT; t0 < ke; t0 += step) {
+        if constexpr (UNIFORM_PAGE) {
+            if (pf_t == ta + sub * TT) {
+#pragma unroll
+                for (int s = 0; s < kSubTiles<U>; ++s) pages[s] = pf_pages[s];
+            } else {
+                tile_pages<U>(pages, a, tbl, ta + sub * TT, tb);
+            }
+        }
+        pf_t = -1;
+        for (int t0 = ta + sub * TT; t0 < tb; t0 += step) {
             Words<KW> kr[U], vr[U];
-            if (t0 + TT <= ke) {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, pages, kc, vc, t0, ke, row, lane_off,
+            if (t0 + TT <= tb) {
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, pages, kc, vc, t0, tb, row, lane_off,
                                                               head_off, tok_bytes, clamp_off, bad);
             } else {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, pages, kc, vc, t0, ke, row,
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, pages, kc, vc, t0, tb, row,
                                                                lane_off, head_off, tok_bytes, clamp_off, bad);
             }
-            if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, t0 + step, ke);
+            if constexpr (UNIFORM_PAGE) {
+                if (t0 + step < tb) {
+                    tile_pages<U>(pages, a, tbl, t0 + step, tb);
+                } else if (next >= kb && next < ke) {
+                    pf_t = next + sub * TT;
+                    tile_pages<U>(pf_pages, a, tbl, pf_t, ke);
+                }
+            }
             process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale,
-                                                      t0 + my_tok < ke, col);
+                                                      t0 + my_tok < tb, col);
         }
+    }
 
+    __device__ __forceinline__ void flush(const AttnArgs& a, DecodeLds<D, G, NW>& lds, bool direct, int prow) {
         // per-head (max, sum) of this row, in every lane of the row
         float m[G], l[G];
         static_for<G>([&](auto g) {
@@ -359,7 +407,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         });
 
         // merge the four rows of the wave
-        bad = __any(bad) || n_dev != n;
+        bool bd = __any(bad) || n_dev != n;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float M = rows4_max(m[g]);
@@ -385,7 +433,7 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
                     lds.ml[wave][g][0] = m[g];
                     lds.ml[wave][g][1] = l[g];
                 }
-                lds.bad[wave] = bad ? 1 : 0;
+                lds.bad[wave] = bd ? 1 : 0;
             }
             __syncthreads();
             if (sub == 0) {
@@ -409,35 +457,53 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[g][e] = at[e];
                 }
-                for (int w = 1; w < tp; ++w) bad |= lds.bad[wave + w] != 0;
+                for (int w = 1; w < tp; ++w) bd |= lds.bad[wave + w] != 0;
             }
         }
 
         if (sub == 0 && row == 0) {
+            const int64_t hq_d = static_cast<int64_t>(a.hq) * D;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 const int hq_idx = h * G + g;
                 const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
                 float o[EPL];
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = bad ? NAN : acc[g][e] * inv;
-                if (un.prow < 0) {
+                for (int e = 0; e < EPL; ++e) o[e] = bd ? NAN : acc[g][e] * inv;
+                if (direct) {
                     char* dst = static_cast<char*>(a.out) +
                                 (static_cast<int64_t>(un.row0) * hq_d + static_cast<int64_t>(hq_idx) * D + col * EPL) * QB;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) o[e] *= a.v_scale;
                     store_out<QDT, EPL>(dst, o);
                 } else {
-                    float* dst = a.partial_o + (static_cast<int64_t>(un.prow) * a.hq + hq_idx) * D + col * EPL;
+                    float* dst = a.partial_o + (static_cast<int64_t>(prow) * a.hq + hq_idx) * D + col * EPL;
 #pragma unroll
                     for (int e = 0; e < EPL; e += 4)
                         *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
                     if (col == 0)
-                        a.partial_lse[static_cast<int64_t>(un.prow) * a.hq + hq_idx] =
-                            bad ? NAN : (l[g] > 0.f ? m[g] + __log2f(l[g]) : -INFINITY);
+                        a.partial_lse[static_cast<int64_t>(prow) * a.hq + hq_idx] =
+                            bd ? NAN : (l[g] > 0.f ? m[g] + __log2f(l[g]) : -INFINITY);
                 }
             }
         }
+    }
+};
+
+// Whether a decode unit covers its sequence's whole key range (its result is
+// the output row).
+__device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.kv_begin == 0 && u.kv_end >= u.pos0 + 1; }
+
+// One decode unit, all of it, on the calling workgroup: every kv head, whole
+// units to the output row, pieces to their partial row.
+template <int QDT, int KVDT, int D, int G, int NW, bool UNIFORM_PAGE>
+__device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, DecodeLds<D, G, NW>& lds) {
+    DecodeRun<QDT, KVDT, D, G, NW, UNIFORM_PAGE> run(a);
+    const bool direct = unit_is_whole(un);
+    for (int h = run.head0; h < a.hkv; h += run.hstep) {
+        run.open(a, un, h);
+        run.tiles(a, run.kb, run.ke);
+        run.flush(a, lds, direct, un.prow);
     }
 }
 
