@@ -91,6 +91,7 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     a.hkv = hkv;
     a.num_blocks = num_blocks;
     a.block_size = block_size;
+    a.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(static_cast<uint32_t>(block_size)) : -1;
     a.qk_scale = scale * (fp8 ? k_scale : 1.f) * kLog2e;
     a.v_scale = fp8 ? v_scale : 1.f;
     a.units = reinterpret_cast<const Unit*>(ws + plan->off_units);

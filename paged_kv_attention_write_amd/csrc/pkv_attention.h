@@ -21,6 +21,7 @@ struct AttnArgs {
     int32_t hkv;
     int64_t num_blocks;
     int32_t block_size;
+    int32_t block_shift;          // log2(block_size) when a power of two, else -1
     float qk_scale;               // scale * k_scale * log2(e): scores in log2 units
     float v_scale;                // applied to the final output
     const Unit* units;
@@ -28,6 +29,13 @@ struct AttnArgs {
     float* partial_o;             // [rows][hq][D]
     float* partial_lse;           // [rows][hq], log2 units
 };
+
+// Index in the block table of the page holding token t, and t's row in it
+// (shifts for a power-of-two page size, else a division).
+__device__ __forceinline__ int page_of(const AttnArgs& a, int t) {
+    return a.block_shift >= 0 ? t >> a.block_shift : t / a.block_size;
+}
+__device__ __forceinline__ int row_in_page(const AttnArgs& a, int t, int pidx) { return t - pidx * a.block_size; }
 
 __device__ __forceinline__ Unit load_unit(const_ptr<Unit> units, int i) {
     const const_ptr<int32_t> w = reinterpret_cast<const_ptr<int32_t>>(units + i);

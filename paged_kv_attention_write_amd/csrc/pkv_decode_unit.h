@@ -115,14 +115,30 @@ __device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const
 #pragma unroll
     for (int s = 0; s < kSubTiles<U>; ++s) {
         const int ts = t0 + 16 * s;
-        const int pidx = ts / a.block_size;
+        const int pidx = page_of(a, ts);
         pages[s] = (ts < ke && pidx < a.max_blocks) ? tbl[pidx] : -1;
+    }
+}
+
+// Per-token pages: the table entries of this lane's tokens t0 + 4u + row of
+// the wave-tile at t0 (tokens at or past lim take the piece's last key),
+// read unconditionally at a clamped index.  (Reading them a tile ahead was
+// measured slower on one-token pages.)
+template <int U>
+__device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, const_ptr<int32_t> tbl, int t0,
+                                           int lim, int ke, int row) {
+    const int last = page_of(a, ke - 1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int t = t0 + 4 * u + row;
+        const int pidx = t < lim ? page_of(a, t) : last;
+        lp[u] = tbl[min(pidx, a.max_blocks - 1)];
     }
 }
 
 template <int KVDT, int D, int U, int KW, bool UNIFORM_PAGE, bool FULL>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
-                                          const_ptr<int32_t> tbl, const int32_t (&pages)[kSubTiles<U>],
+                                          const int32_t (&pages)[kSubTiles<U>], const int32_t (&lp)[U],
                                           const char* kc, const char* vc, int t0, int ke, int row, uint32_t lane_off,
                                           uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, bool& bad) {
     const int bs = a.block_size;
@@ -134,14 +150,14 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
             const int ts = t0 + 16 * s;
-            const int pidx = ts / bs;
+            const int pidx = page_of(a, ts);
             const bool in = FULL || ts < ke;
             const uint32_t page = static_cast<uint32_t>(pages[s]);
             const bool pok = page < nblocks;  // a negative id wraps to >= 2^31
             if (in && !pok) bad = true;
             const int64_t slot0 =
                 pok ? static_cast<int64_t>(static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
-                                           static_cast<uint32_t>(ts - pidx * bs))
+                                           static_cast<uint32_t>(row_in_page(a, ts, pidx)))
                     : 0;
             const char* kb = kc + slot0 * tok_bytes;
             const char* vb = vc + slot0 * tok_bytes;
@@ -161,19 +177,18 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
             }
         }
     } else {
-        // one lookup per token: lane row r reads the page of token t0 + 4u + r;
-        // the table is read at a clamped index, unconditionally
-        const int last_pidx = (ke - 1) / bs;
+        // one page per token: lane row r takes the page of token t0 + 4u + r
+        // from lp
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = t0 + 4 * u + row;
             const bool tv = FULL || t < ke;
-            const int pidx = tv ? t / bs : last_pidx;
-            const uint32_t page = static_cast<uint32_t>(tbl[min(pidx, a.max_blocks - 1)]);
+            const int pidx = page_of(a, t);
+            const uint32_t page = static_cast<uint32_t>(lp[u]);
             const bool ok = tv && pidx < a.max_blocks && page < nblocks;  // a negative id wraps to >= 2^31
             bad |= tv && !ok;
             const uint64_t slot = static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
-                                  static_cast<uint32_t>(t - pidx * bs);
+                                  static_cast<uint32_t>(row_in_page(a, t, pidx));
             const int64_t off = ok ? static_cast<int64_t>(slot) * tok_bytes + head_off : clamp_off;
             k[u] = load_words<KW>(kc + off);
             v[u] = load_words<KW>(vc + off);
@@ -189,11 +204,11 @@ __device__ __forceinline__ int64_t clamp_offset(const AttnArgs& a, const_ptr<int
     const int bs = a.block_size;
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     const int t = ke - 1;
-    const int pidx = t / bs;
+    const int pidx = page_of(a, t);
     const uint32_t page = static_cast<uint32_t>(pidx < a.max_blocks ? tbl[pidx] : -1);
     if (page >= nblocks) return head_off;
     return static_cast<int64_t>(static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
-                                static_cast<uint32_t>(t - pidx * bs)) * tok_bytes + head_off;
+                                static_cast<uint32_t>(row_in_page(a, t, pidx))) * tok_bytes + head_off;
 }
 
 // Scores in log2 units above the running maximum by at most this much are
@@ -367,6 +382,7 @@ struct DecodeRun {
         // while this tile is computed, so the next tile's K/V loads need not
         // wait for a table read.
         int32_t pages[kSubTiles<U>];
+        int32_t lp[U];  // per-token pages: this lane's table entries
         if constexpr (UNIFORM_PAGE) {
             if (pf_t == ta + sub * TT) {
 #pragma unroll
@@ -378,12 +394,13 @@ struct DecodeRun {
         pf_t = -1;
         for (int t0 = ta + sub * TT; t0 < tb; t0 += step) {
             Words<KW> kr[U], vr[U];
+            if constexpr (!UNIFORM_PAGE) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
             if (t0 + TT <= tb) {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, tbl, pages, kc, vc, t0, tb, row, lane_off,
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
                                                               head_off, tok_bytes, clamp_off, bad);
             } else {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, tbl, pages, kc, vc, t0, tb, row,
-                                                               lane_off, head_off, tok_bytes, clamp_off, bad);
+                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
+                                                               head_off, tok_bytes, clamp_off, bad);
             }
             if constexpr (UNIFORM_PAGE) {
                 if (t0 + step < tb) {

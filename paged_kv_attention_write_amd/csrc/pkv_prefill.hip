@@ -94,7 +94,7 @@ struct PfRole {
 
 // Page id of the thread's key in the tile at t0, or -1 (past kend or the table).
 __device__ __forceinline__ int32_t pf_page(const AttnArgs& a, const_ptr<int32_t> tbl, int t, int kend) {
-    const int pidx = t / a.block_size;
+    const int pidx = page_of(a, t);
     return (t < kend && pidx < a.max_blocks) ? tbl[pidx] : -1;
 }
 
@@ -117,8 +117,8 @@ __device__ __forceinline__ void pf_load(PfRegs<KVDT, D>& r, const AttnArgs& a, c
     const bool tv = role.active && t < kend;
     const bool ok = tv && static_cast<uint32_t>(page) < nblocks;  // a negative id wraps to >= 2^31
     bad |= tv && !ok;
-    const int pidx = t / a.block_size;
-    const int64_t slot = static_cast<int64_t>(page) * a.block_size + (t - pidx * a.block_size);
+    const int pidx = page_of(a, t);
+    const int64_t slot = static_cast<int64_t>(page) * a.block_size + row_in_page(a, t, pidx);
     const int64_t off = ok ? ((slot * a.hkv + h) * D + role.dg * 8) * KVB : 0;
     r.k = load_words<W>(static_cast<const char*>(a.k_cache) + off);
     r.v = load_words<W>(static_cast<const char*>(a.v_cache) + off);
