@@ -10,7 +10,7 @@
 // piece.  Its kPrefillQRows (row, q head) pairs are spread over the 8 waves,
 // 16 per wave: pair x = 16 w + n is row x / G, q head h G + x % G, so the G
 // heads that share K/V sit side by side.  Per tile of 32 keys the workgroup
-// stages K and V row-major in LDS, then every wave computes, with
+// stages K and V in LDS, then every wave computes, with
 // v_mfma_f32_16x16x32_bf16,
 //   S^T[key][pair] = K Q^T   (A = K from LDS, B = its q slice in registers)
 //   O^T[d][pair]  += V^T P^T (A = V^T read from the row-major V tile with the
@@ -25,10 +25,11 @@
 // causally: row r of the chunk sits at position pos0 + r and sees keys up to
 // it.  fp8 K/V are widened to bf16 (exactly) when staged.
 //
-// Pipeline per tile: the K/V loads of tiles t + 1 and t + 2 and the page
-// ids of tiles t + 3 and t + 4 are in flight while tile t is computed from
-// one LDS buffer; tile t + 1 is then staged into the other buffer, and one
-// barrier closes the step.
+// Two staging paths feed the same tile code: a ring of four LDS stages
+// filled by direct-to-LDS loads (bf16 K/V, D = 128, pages of a power of two
+// >= 16 tokens) and two padded LDS buffers filled from registers (every other
+// case).  Both keep the loads of later tiles in flight while tile t is
+// computed and close each step with one barrier.
 #include <math.h>
 
 #include "pkv_decode_unit.h"
@@ -92,10 +93,12 @@ struct PfRole {
     }
 };
 
-// Page id of the thread's key in the tile at t0, or -1 (past kend or the table).
-__device__ __forceinline__ int32_t pf_page(const AttnArgs& a, const_ptr<int32_t> tbl, int t, int kend) {
-    const int pidx = page_of(a, t);
-    return (t < kend && pidx < a.max_blocks) ? tbl[pidx] : -1;
+// Table entry of the page of key t, read unconditionally at an index clamped
+// into the sequence's row (max_blocks >= 1): every thread issues the same
+// loads in the same order, so the waits for them count in order and none is
+// taken right after its load.  pf_load decides whether the entry is valid.
+__device__ __forceinline__ int32_t pf_page(const AttnArgs& a, const_ptr<int32_t> tbl, int t) {
+    return tbl[min(page_of(a, t), a.max_blocks - 1)];
 }
 
 template <int KVDT, int D>
@@ -104,7 +107,7 @@ struct PfRegs {
     bool ok;
 };
 
-// Issue the K/V loads of the thread's key t (page id given).  Loads are
+// Issue the K/V loads of the thread's key t (its table entry given).  Loads are
 // never skipped: a key past kend or on a page outside the pool reads the
 // first bytes of the pool instead (the pool holds at least one block), is
 // staged as zeros, and a page outside the pool flags the unit.
@@ -114,10 +117,11 @@ __device__ __forceinline__ void pf_load(PfRegs<KVDT, D>& r, const AttnArgs& a, c
     constexpr int KVB = dt_bytes(KVDT);
     constexpr int W = PfItem<KVDT>::W;
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
-    const bool tv = role.active && t < kend;
-    const bool ok = tv && static_cast<uint32_t>(page) < nblocks;  // a negative id wraps to >= 2^31
-    bad |= tv && !ok;
     const int pidx = page_of(a, t);
+    const bool tv = role.active && t < kend;
+    // a key past the table, or a negative id (wraps to >= 2^31), is invalid
+    const bool ok = tv && pidx < a.max_blocks && static_cast<uint32_t>(page) < nblocks;
+    bad |= tv && !ok;
     const int64_t slot = static_cast<int64_t>(page) * a.block_size + row_in_page(a, t, pidx);
     const int64_t off = ok ? ((slot * a.hkv + h) * D + role.dg * 8) * KVB : 0;
     r.k = load_words<W>(static_cast<const char*>(a.k_cache) + off);
@@ -152,25 +156,76 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(uint2, r);
 }
 
+// LDS views of one staged tile; rows are addressed as (16-row block, row in
+// block).  The register-staged path keeps row-major rows padded by kPfPad
+// elements.  A ring stage of the direct-to-LDS path (D = 128) is 16 slots of
+// kRingSlotElems elements (1 KiB + 32 bytes): slot 8 f + i holds, as four
+// 256-byte rows j = 0..3, the K rows of keys 16 f + i and 16 f + i + 8 and
+// then the V rows of the same two keys, the 16-byte chunk c of row j stored
+// at c ^ (j & 1).  The padding and the swap make the 16 rows of a K operand
+// read and each 32-lane half of a transposing V read fall in distinct banks,
+// and every read of a lane sits at a constant offset from one address.
+//
+// A view gives a lane's operand addresses as one per-lane pointer plus
+// compile-time offsets: k_lane(n, g4) + k_off(kb2, s) is the K operand of
+// pair column n, lane group g4, key block kb2 and k step s (keys 16 kb2 + n,
+// elements 32 s + 8 g4 .. + 7); v_lane(n, g4) + v_off(hi, b) the 4-element
+// piece of the V^T operand (key 16 hi + 4 g4 + n / 4, elements
+// 16 b + 4 (n % 4) .. + 3).
+template <int D>
+struct PaddedTile {
+    const uint16_t* k;
+    const uint16_t* v;
+    static constexpr int kRow = D + kPfPad;
+    __device__ const uint16_t* k_lane(int n, int g4) const { return k + n * kRow + 8 * g4; }
+    static constexpr int k_off(int kb2, int s) { return 16 * kb2 * kRow + 32 * s; }
+    __device__ const uint16_t* v_lane(int n, int g4) const { return v + (4 * g4 + (n >> 2)) * kRow + 4 * (n & 3); }
+    static constexpr int v_off(int hi, int b) { return 16 * hi * kRow + 16 * b; }
+};
+
+constexpr int kRingSlotElems = 528;
+constexpr int kRingStageElems = 16 * kRingSlotElems;  // K and V of one tile
+
+struct RingTile {
+    const uint16_t* st;
+    // key r < 16 of a half, row j = r / 8 (+ 2 for V) of slot r % 8
+    __device__ const uint16_t* k_lane(int n, int g4) const {
+        const int jr = n >> 3;
+        return st + (n & 7) * kRingSlotElems + jr * 128 + 8 * (g4 ^ jr);
+    }
+    static constexpr int k_off(int kb2, int s) { return 8 * kRingSlotElems * kb2 + 32 * s; }
+    __device__ const uint16_t* v_lane(int n, int g4) const {
+        const int key = 4 * g4 + (n >> 2);
+        const int jr = key >> 3;
+        return st + (key & 7) * kRingSlotElems + (2 + jr) * 128 + 8 * (((n >> 1) & 1) ^ jr) + 4 * (n & 1);
+    }
+    static constexpr int v_off(int hi, int b) { return 8 * kRingSlotElems * hi + 16 * b; }
+};
+
 // One tile of one wave: S^T for keys t0 + 16 kb2 + 4 g4 + i of pair n, the
 // online softmax update, and O^T += V^T P^T.  qk = |scale * k_scale * log2 e|
 // (a negative factor is carried by the sign of q, and qk >= 2^-100).  mask
 // (uniform in the wave): the tile crosses the causal diagonal, the end of the
 // key range or rows past the unit, so keys are tested one by one; otherwise
-// every key of the tile is visible to every pair of the wave.  Per score the vector work is one fma into one v_exp_f32,
-// a share of a max3, a packed bf16 conversion and a dot2 into the row sum.
-template <int D, int NS = D / 32, int ND = D / 16>
-__device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, int t0, int kend, int pos, bool row_ok,
-                                           bool mask, int n, int g4, float qk, const bf16x8_t (&qb)[NS],
-                                           f32x4_t (&acc)[ND], float& m_run, float& l_run) {
+// every key of the tile is visible to every pair of the wave.  Per score the
+// vector work is one fma into one v_exp_f32, a share of a max tree, a packed
+// bf16 conversion and a dot2 into the row sum.  The first VH blocks of the V
+// operand are read before the softmax so that the reads overlap it.
+template <int D, int VH, class Tile>
+__device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, int pos, bool row_ok, bool mask, int n,
+                                           int g4, float qk, const bf16x8_t (&qb)[D / 32], f32x4_t (&acc)[D / 16],
+                                           float& m_run, float& l_run) {
+    constexpr int NS = D / 32;
+    constexpr int ND = D / 16;
+    const uint16_t* const kl = T.k_lane(n, g4);
+    const uint16_t* const vl = T.v_lane(n, g4);
     float sv[8];  // raw q.k
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_bf16x8(&lds.k[buf][16 * kb2 + n][32 * s + 8 * g4]), qb[s],
-                                                        c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_bf16x8(kl + Tile::k_off(kb2, s)), qb[s], c, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[4 * kb2 + i] = c[i];
     }
@@ -181,14 +236,29 @@ __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, in
             sv[j] = (row_ok && kp < kend && kp <= pos) ? sv[j] : -INFINITY;
         }
     }
-    float mr = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mr = fmaxf(mr, __shfl_xor(mr, 16));
-    mr = fmaxf(mr, __shfl_xor(mr, 32));
-    const float mt = (mr == -INFINITY) ? -INFINITY : mr * qk;  // the tile's max in log2 units
-    // lazy rescale, as in the decode unit: scores at most 2^8 above the
-    // running maximum are taken against it
-    const bool need = mt > m_run + 8.0f;
-    if (__any(need)) {
+    // V^T operand: lane group g4 takes keys 4 g4 + j (j < 4) and 16 + 4 g4 +
+    // j - 4 (j >= 4), where the first product left their scores; lane 4 j + q
+    // of the group points at V[key_j][16 b + 4 q].
+    auto v_operand = [&](int b) {
+        const uint2 lo = lds_read_tr16(vl + Tile::v_off(0, b));
+        const uint2 hi = lds_read_tr16(vl + Tile::v_off(1, b));
+        return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    bf16x8_t va[VH > 0 ? VH : 1];
+#pragma unroll
+    for (int b = 0; b < VH; ++b) va[b] = v_operand(b);
+    // Lazy rescale, as in the decode unit: scores at most 2^8 above the
+    // running maximum are taken against it.  The running maximum is shared by
+    // the four lanes of a pair, so while no lane's own tile maximum passes it
+    // by more than 8 (log2) nothing is exchanged; otherwise the pair's
+    // maximum is formed across its lanes and the pair rescales.
+    const float ml = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    const float mtl = (ml == -INFINITY) ? -INFINITY : ml * qk;  // this lane's tile maximum in log2 units
+    if (__any(mtl > m_run + 8.0f)) {
+        float mr = fmaxf(ml, __shfl_xor(ml, 16));
+        mr = fmaxf(mr, __shfl_xor(mr, 32));
+        const float mt = (mr == -INFINITY) ? -INFINITY : mr * qk;  // the pair's tile maximum
+        const bool need = mt > m_run + 8.0f;
         const float m_new = need ? mt : m_run;
         const float alpha = need ? exp2_fast(m_run - m_new) : 1.f;
         l_run *= alpha;
@@ -210,31 +280,130 @@ __device__ __forceinline__ void pf_compute(const PrefillLds<D>& lds, int buf, in
         const bf16x2_t pp = {pb[2 * j], pb[2 * j + 1]};
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
     }
-    // V^T operand: lane group g4 takes keys 4 g4 + j (j < 4) and 16 + 4 g4 +
-    // j - 4 (j >= 4), where the first product left their scores; lane 4 j + q
-    // of the group points at V[key_j][16 b + 4 q]
-    const int vkey = 4 * g4 + (n >> 2);
-    const int vcol = 4 * (n & 3);
 #pragma unroll
-    for (int b = 0; b < ND; ++b) {
-        const uint2 lo = lds_read_tr16(&lds.v[buf][vkey][16 * b + vcol]);
-        const uint2 hi = lds_read_tr16(&lds.v[buf][16 + vkey][16 * b + vcol]);
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[b], 0, 0, 0);
-    }
+    for (int b = 0; b < ND; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b < VH ? va[b < VH ? b : 0] : v_operand(b), pb, acc[b], 0, 0,
+                                                         0);
 }
 
-// The prefill units of plan queue `queue` on the calling workgroup.
+// One wave's share of a prefill unit: its 16 (row, q head) pairs, their q
+// slices, the running softmax state and the O^T accumulator, and the unit's
+// key range.  open() reads the unit and the q slices; close() writes the
+// output (uncut unit) or the normalised partial and its LSE (cut unit) once
+// the workgroup has agreed on `bad`.
+template <int D, int G>
+struct PfWave {
+    static constexpr int NS = D / 32;  // k steps of the first product
+    static constexpr int ND = D / 16;  // 16-row blocks of O^T
+    int n, g4, r, hq_idx, pos, h, kb, kend;
+    bool row_ok, wave_has_rows, wave_full;
+    int wave_first_pos, wave_last_pos;
+    const_ptr<int32_t> tbl;
+    bf16x8_t qb[NS];
+    float qk;
+    f32x4_t acc[ND];
+    float m_run, l_run;
+    bool bad;
+
+    __device__ __forceinline__ void open(const AttnArgs& a, const Unit& un, int wave, int lane) {
+        constexpr int QB = 2;  // bf16 queries
+        n = lane & 15;         // pair column of this lane
+        g4 = lane >> 4;
+        h = un.kind - kUnitPrefill;
+        const int x = wave * kPfPairsPerWave + n;
+        r = x / G;  // row of the chunk block
+        hq_idx = h * G + x % G;
+        row_ok = r < un.nrows;
+        pos = un.pos0 + r;
+        // rows of this wave: positions pos0 + wr0 .. pos0 + wr1
+        const int wr0 = (wave * kPfPairsPerWave) / G;
+        const int wr1 = min(un.nrows - 1, (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G);
+        wave_has_rows = wr0 < un.nrows;
+        wave_last_pos = un.pos0 + wr1;
+        wave_first_pos = un.pos0 + wr0;
+        // every pair of the wave is a row of the unit
+        wave_full = (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G < un.nrows;
+
+        const int n_ctx = as_const(a.context_lens)[un.seq];
+        kb = un.kv_begin;
+        kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
+        tbl = as_const(a.block_tables) + static_cast<int64_t>(un.seq) * a.max_blocks;
+
+        // q slice of this lane's pair: elements 32 s + 8 g4 .. + 7
+        const char* qrow = static_cast<const char*>(a.q) +
+                           (static_cast<int64_t>(un.row0 + r) * a.q_stride + static_cast<int64_t>(hq_idx) * D) * QB;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            Words<4> w;
+            if (row_ok) {
+                w = load_words<4>(qrow + (32 * s + 8 * g4) * QB);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w.w[j] = 0u;
+            }
+            // a negative score factor is carried by the sign of q (exact)
+            const uint32_t flip = a.qk_scale < 0.f ? 0x80008000u : 0u;
+            qb[s] = __builtin_bit_cast(bf16x8_t,
+                                       make_uint4(w.w[0] ^ flip, w.w[1] ^ flip, w.w[2] ^ flip, w.w[3] ^ flip));
+        }
+        // |factor|, at least 2^-100 so that -inf * qk stays -inf (a zero
+        // factor then still gives exp2 of exactly 0 for every visible key)
+        qk = fmaxf(fabsf(a.qk_scale), 0x1p-100f);
+#pragma unroll
+        for (int b = 0; b < ND; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;  // running max of this lane's pair (its four lanes agree)
+        l_run = 0.f;        // this lane's share of the running sum
+        bad = false;
+    }
+
+    __device__ __forceinline__ bool computes(int t0) const { return wave_has_rows && t0 <= wave_last_pos; }
+    __device__ __forceinline__ bool masked(int t0) const {
+        return !(wave_full && t0 + kPfKeys <= kend && t0 + kPfKeys - 1 <= wave_first_pos);
+    }
+    template <int VH, class Tile>
+    __device__ __forceinline__ void tile(const Tile& T, int t0) {
+        if (computes(t0)) pf_compute<D, VH>(T, t0, kend, pos, row_ok, masked(t0), n, g4, qk, qb, acc, m_run, l_run);
+    }
+
+    __device__ __forceinline__ void close(const AttnArgs& a, const Unit& un) {
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (!row_ok) return;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (un.prow < 0) {
+            uint16_t* dst =
+                static_cast<uint16_t*>(a.out) + (static_cast<int64_t>(un.row0 + r) * a.hq + hq_idx) * D + 4 * g4;
+            const float sc = inv * a.v_scale;
+#pragma unroll
+            for (int b = 0; b < ND; ++b) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = bad ? NAN : acc[b][i] * sc;
+                store_out<PKV_DTYPE_BF16, 4>(reinterpret_cast<char*>(dst + 16 * b), o);
+            }
+        } else {
+            const int64_t prow = static_cast<int64_t>(un.prow) + r;
+            float* dst = a.partial_o + (prow * a.hq + hq_idx) * D + 4 * g4;
+#pragma unroll
+            for (int b = 0; b < ND; ++b) {
+                const float4 o = bad ? make_float4(NAN, NAN, NAN, NAN)
+                                     : make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv,
+                                                   acc[b][3] * inv);
+                *reinterpret_cast<float4*>(dst + 16 * b) = o;
+            }
+            if (g4 == 0)
+                a.partial_lse[prow * a.hq + hq_idx] = bad ? NAN : (l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY);
+        }
+    }
+};
+
+// The prefill units of plan queue `queue` on the calling workgroup, K/V
+// staged through registers into two padded LDS buffers (any page size, bf16
+// or fp8 K/V, D = 64 or 128).
 template <int KVDT, int D, int G>
 __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, PrefillLds<D>& lds) {
-    constexpr int QB = 2;       // bf16 queries
-    constexpr int NS = D / 32;  // k steps of the first product
-    constexpr int ND = D / 16;  // 16-row blocks of O^T
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int n = lane & 15;  // pair column of this lane
-    const int g4 = lane >> 4;
     const PfRole<D> role;
 
     const const_ptr<Unit> units = as_const(a.units);
@@ -243,70 +412,23 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
     const int u_end = qoff[queue + 1];
     for (int ui = u_begin; ui < u_end; ++ui) {
         const Unit un = load_unit(units, ui);
-        const int h = un.kind - kUnitPrefill;
-        const int x = wave * kPfPairsPerWave + n;
-        const int r = x / G;  // row of the chunk block
-        const int hq_idx = h * G + x % G;
-        const bool row_ok = r < un.nrows;
-        const int pos = un.pos0 + r;
-        // rows of this wave: positions pos0 + wr0 .. pos0 + wr1
-        const int wr0 = (wave * kPfPairsPerWave) / G;
-        const int wr1 = min(un.nrows - 1, (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G);
-        const bool wave_has_rows = wr0 < un.nrows;
-        const int wave_last_pos = un.pos0 + wr1;
-        const int wave_first_pos = un.pos0 + wr0;
-        // every pair of the wave is a row of the unit
-        const bool wave_full = (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G < un.nrows;
-
-        const int n_ctx = as_const(a.context_lens)[un.seq];
-        const int kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
-        const const_ptr<int32_t> tbl = as_const(a.block_tables) + static_cast<int64_t>(un.seq) * a.max_blocks;
-
-        // q slice of this lane's pair: elements 32 s + 8 g4 .. + 7
-        bf16x8_t qb[NS];
-        {
-            const char* qrow = static_cast<const char*>(a.q) +
-                               (static_cast<int64_t>(un.row0 + r) * a.q_stride + static_cast<int64_t>(hq_idx) * D) * QB;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                Words<4> w;
-                if (row_ok) {
-                    w = load_words<4>(qrow + (32 * s + 8 * g4) * QB);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) w.w[j] = 0u;
-                }
-                // a negative score factor is carried by the sign of q (exact)
-                const uint32_t flip = a.qk_scale < 0.f ? 0x80008000u : 0u;
-                qb[s] = __builtin_bit_cast(bf16x8_t, make_uint4(w.w[0] ^ flip, w.w[1] ^ flip, w.w[2] ^ flip,
-                                                                w.w[3] ^ flip));
-            }
-        }
-        // |factor|, at least 2^-100 so that -inf * qk stays -inf (a zero
-        // factor then still gives exp2 of exactly 0 for every visible key)
-        const float qk = fmaxf(fabsf(a.qk_scale), 0x1p-100f);
-
-        f32x4_t acc[ND];
-#pragma unroll
-        for (int b = 0; b < ND; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY;  // running max of this lane's pair (its four lanes agree)
-        float l_run = 0.f;        // this lane's share of the running sum
-        bool bad = false;
+        PfWave<D, G> W;
+        W.open(a, un, wave, lane);
+        const int kb = W.kb, kend = W.kend, h = W.h;
+        const const_ptr<int32_t> tbl = W.tbl;
 
         // prologue: tile 0 staged; tiles 1 and 2 and the pages of tiles 3
         // and 4 in flight
-        const int kb = un.kv_begin;
-        const int kend_role = role.active ? kend : 0;  // idle staging threads look nothing up
         PfRegs<KVDT, D> ra, rb;
         __syncthreads();  // the LDS of the previous unit is free
-        pf_load<KVDT, D>(ra, a, role, h, kb + role.kk, kend, pf_page(a, tbl, kb + role.kk, kend_role), bad);
+        pf_load<KVDT, D>(ra, a, role, h, kb + role.kk, kend, pf_page(a, tbl, kb + role.kk), W.bad);
         pf_stage<KVDT, D>(ra, role, lds, 0);
-        pf_load<KVDT, D>(ra, a, role, h, kb + kPfKeys + role.kk, kend,
-                         pf_page(a, tbl, kb + kPfKeys + role.kk, kend_role), bad);
+        pf_load<KVDT, D>(ra, a, role, h, kb + kPfKeys + role.kk, kend, pf_page(a, tbl, kb + kPfKeys + role.kk),
+                         W.bad);
         pf_load<KVDT, D>(rb, a, role, h, kb + 2 * kPfKeys + role.kk, kend,
-                         pf_page(a, tbl, kb + 2 * kPfKeys + role.kk, kend_role), bad);
-        int32_t pa = pf_page(a, tbl, kb + 3 * kPfKeys + role.kk, kend_role);
-        int32_t pb = pf_page(a, tbl, kb + 4 * kPfKeys + role.kk, kend_role);
+                         pf_page(a, tbl, kb + 2 * kPfKeys + role.kk), W.bad);
+        int32_t pa = pf_page(a, tbl, kb + 3 * kPfKeys + role.kk);
+        int32_t pb = pf_page(a, tbl, kb + 4 * kPfKeys + role.kk);
         __syncthreads();
 
         // Two phases per trip so that the two register sets take turns: the
@@ -314,16 +436,15 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
         // (loaded two phases ago) into the other buffer and reloads its
         // register set with tile t + 3.
         auto phase = [&](int t0, int buf, PfRegs<KVDT, D>& rs, int32_t& pg) {
-            if (wave_has_rows && t0 <= wave_last_pos) {
-                const bool mask = !(wave_full && t0 + kPfKeys <= kend && t0 + kPfKeys - 1 <= wave_first_pos);
-                pf_compute<D>(lds, buf, t0, kend, pos, row_ok, mask, n, g4, qk, qb, acc, m_run, l_run);
-            }
-            if (t0 + kPfKeys < kend) {
-                pf_stage<KVDT, D>(rs, role, lds, buf ^ 1);
-                const int t3 = t0 + 3 * kPfKeys + role.kk;
-                pf_load<KVDT, D>(rs, a, role, h, t3, kend, pg, bad);
-                pg = pf_page(a, tbl, t3 + 2 * kPfKeys, kend_role);
-            }
+            W.template tile<D / 32>(PaddedTile<D>{&lds.k[buf][0][0], &lds.v[buf][0][0]}, t0);
+            // unconditional, also past the last tile: the other buffer is
+            // free (every wave passed the previous barrier) and every address
+            // stays in bounds, so the loads keep one fixed order and their
+            // waits count in order
+            pf_stage<KVDT, D>(rs, role, lds, buf ^ 1);
+            const int t3 = t0 + 3 * kPfKeys + role.kk;
+            pf_load<KVDT, D>(rs, a, role, h, t3, kend, pg, W.bad);
+            pg = pf_page(a, tbl, t3 + 2 * kPfKeys);
             __syncthreads();
         };
         for (int t0 = kb; t0 < kend; t0 += 2 * kPfKeys) {
@@ -331,79 +452,237 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
             if (t0 + kPfKeys >= kend) break;
             phase(t0 + kPfKeys, 1, rb, pb);
         }
-        bad = __syncthreads_or(bad) != 0;
-
-        float l_tot = l_run + __shfl_xor(l_run, 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        if (row_ok) {
-            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-            if (un.prow < 0) {
-                uint16_t* dst = static_cast<uint16_t*>(a.out) +
-                                (static_cast<int64_t>(un.row0 + r) * a.hq + hq_idx) * D + 4 * g4;
-                const float sc = inv * a.v_scale;
-#pragma unroll
-                for (int b = 0; b < ND; ++b) {
-                    float o[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = bad ? NAN : acc[b][i] * sc;
-                    store_out<PKV_DTYPE_BF16, 4>(reinterpret_cast<char*>(dst + 16 * b), o);
-                }
-            } else {
-                const int64_t prow = static_cast<int64_t>(un.prow) + r;
-                float* dst = a.partial_o + (prow * a.hq + hq_idx) * D + 4 * g4;
-#pragma unroll
-                for (int b = 0; b < ND; ++b) {
-                    const float4 o = bad ? make_float4(NAN, NAN, NAN, NAN)
-                                         : make_float4(acc[b][0] * inv, acc[b][1] * inv, acc[b][2] * inv,
-                                                       acc[b][3] * inv);
-                    *reinterpret_cast<float4*>(dst + 16 * b) = o;
-                }
-                if (g4 == 0)
-                    a.partial_lse[prow * a.hq + hq_idx] =
-                        bad ? NAN : (l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY);
-            }
-        }
+        W.bad = __syncthreads_or(W.bad) != 0;
+        W.close(a, un);
     }
 }
 
-template <int KVDT, int D, int G>
+// ---------------------------------------------------------------------------
+// Direct-to-LDS path (bf16 K/V, D = 128, block_size a power of two >= 16).
+//
+// A ring of kRingStages LDS stages, each one 32-key tile of K and V in the
+// slot layout above.  Per tile, wave w fills slots w and 8 + w with
+// global_load_lds_dwordx4, which writes LDS without passing through
+// registers: lane l loads the 16 bytes that the layout puts at position l of
+// the slot (16 lanes read one 256-byte row of K or V).  Tile t + 3 is loaded
+// while tile t is computed.  Each step waits (vmcnt) until the wave's own
+// loads of the current tile have landed and then meets the others at a
+// barrier, after which every slot is visible.  The page-table entries come
+// through scalar loads two tiles ahead of their use, so vmcnt counts only the
+// tile loads.  Each 16-key half of a tile lies in one page (tiles start at
+// multiples of 16 keys and pages hold a power of two >= 16 of them), so a
+// slot needs one entry and a tile two.
+// ---------------------------------------------------------------------------
+constexpr int kRingStages = 4;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone; gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0)
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier without a memory fence (the waits before it are
+// explicit); the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+template <int G>
+__device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue, uint16_t* s0, uint16_t* s1,
+                                                   uint16_t* s2, uint16_t* s3) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
+    const int shift = a.block_shift;
+    // this lane's load: slot row j = lane / 16, a K row (j < 2) or a V row
+    // of key w + 8 (j % 2) of a half (rows of the pool are hkv * 256 bytes
+    // apart), logical chunk (lane % 16) ^ (j % 2)
+    const int j = lane >> 4;
+    const char* const lane_src = static_cast<const char*>(j < 2 ? a.k_cache : a.v_cache) +
+                                 static_cast<uint32_t>(wave + 8 * (j & 1)) * static_cast<uint32_t>(a.hkv) * (D * 2) +
+                                 static_cast<uint32_t>(((lane & 15) ^ (j & 1)) * 16);
+    const const_ptr<Unit> units = as_const(a.units);
+    const const_ptr<int32_t> qoff = as_const(a.queue_off);
+    const int u_begin = qoff[queue];
+    const int u_end = qoff[queue + 1];
+    for (int ui = u_begin; ui < u_end; ++ui) {
+        const Unit un = load_unit(units, ui);
+        PfWave<D, G> W;
+        W.open(a, un, wave, lane);
+        const int kb = W.kb, kend = W.kend, h = W.h;
+        const const_ptr<int32_t> tbl = W.tbl;
+        const int ntiles = kend > kb ? (kend - kb + kPfKeys - 1) / kPfKeys : 0;
+        const int glast = kend > kb ? ((kend - 1) & ~15) : kb;  // start of the unit's last 16 keys
+
+        // a half of 16 keys starting at t0 + 16 f, clamped to the last half
+        // (so that a half past kend reads keys that exist), and its
+        // page-table entry (index clamped into the row; validity is decided
+        // at the load)
+        auto half = [&](int t0, int f) { return min(t0 + 16 * f, glast); };
+        auto entry = [&](int t0, int f) { return tbl[min(half(t0, f) >> shift, a.max_blocks - 1)]; };
+        struct Entries {
+            int32_t e0, e1;
+        };
+        auto entries = [&](int t0) { return Entries{entry(t0, 0), entry(t0, 1)}; };
+        auto issue = [&](uint16_t* st, int t0, Entries e) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const int g = half(t0, f);
+                const int32_t ef = f ? e.e1 : e.e0;
+                const int pidx = g >> shift;
+                const bool ok = pidx < a.max_blocks && static_cast<uint32_t>(ef) < nblocks;
+                W.bad |= t0 + 16 * f < kend && !ok;
+                const int64_t row0 = static_cast<int64_t>(ok ? ef : 0) * a.block_size + (g - (pidx << shift));
+                __builtin_amdgcn_global_load_lds(lane_src + (row0 * a.hkv + h) * (D * 2),
+                                                 (lds_void_t*)(st + (8 * f + wave) * kRingSlotElems), 16, 0, 0);
+            }
+        };
+
+        Entries e[kRingStages];  // page entries of the tiles in flight, slot = tile % 4
+        ring_barrier();          // every wave is done with the previous unit's stages
+        e[0] = entries(kb);
+        e[1] = entries(kb + kPfKeys);
+        e[2] = entries(kb + 2 * kPfKeys);
+        if (0 < ntiles) issue(s0, kb, e[0]);
+        if (1 < ntiles) issue(s1, kb + kPfKeys, e[1]);
+        if (2 < ntiles) issue(s2, kb + 2 * kPfKeys, e[2]);
+        e[3] = entries(kb + 3 * kPfKeys);
+        e[0] = entries(kb + 4 * kPfKeys);
+
+        // tile tt from stage cur; tile tt + 3 into stage nxt with entry
+        // use_e; the entry of tile tt + 5 into load_e
+        auto phase = [&](int tt, uint16_t* cur, uint16_t* nxt, Entries use_e, Entries& load_e) {
+            const int t0 = kb + tt * kPfKeys;
+            // this wave's loads of tile tt are in once at most those of the
+            // (up to two) later tiles already issued are still in flight
+            const int later = min(2, ntiles - 1 - tt);
+            if (later >= 2)
+                wait_vmcnt<4>();
+            else if (later == 1)
+                wait_vmcnt<2>();
+            else
+                wait_vmcnt<0>();
+            if (t0 + kPfKeys > kend) {
+                // keys at or past kend were read from inside their page (or
+                // from the last group): zero their V rows so that a zero
+                // weight never meets a non-finite value
+                if (j >= 2) {
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        if (t0 + 16 * f + wave + 8 * (j & 1) >= kend)
+                            *reinterpret_cast<uint4*>(cur + (8 * f + wave) * kRingSlotElems + lane * 8) =
+                                make_uint4(0, 0, 0, 0);
+                }
+                wait_lgkmcnt0();
+            }
+            ring_barrier();
+            if (tt + 3 < ntiles) issue(nxt, t0 + 3 * kPfKeys, use_e);
+            load_e = entries(t0 + 5 * kPfKeys);
+            W.template tile<D / 32>(RingTile{cur}, t0);
+        };
+        for (int tt = 0; tt < ntiles; tt += kRingStages) {
+            phase(tt, s0, s3, e[3], e[1]);
+            if (tt + 1 >= ntiles) break;
+            phase(tt + 1, s1, s0, e[0], e[2]);
+            if (tt + 2 >= ntiles) break;
+            phase(tt + 2, s2, s1, e[1], e[3]);
+            if (tt + 3 >= ntiles) break;
+            phase(tt + 3, s3, s2, e[2], e[0]);
+        }
+        W.bad = __syncthreads_or(W.bad) != 0;
+        W.close(a, un);
+    }
+}
+
+// LDS of the direct-to-LDS path: four stage arrays of their own (so that the
+// compiler sees which stage a read touches); the decode workgroups of a mixed
+// launch use the first one.
+template <int D, int G>
+constexpr int ring_stage0_elems() {
+    return sizeof(DecodeLds<D, G, kPfWaves>) / 2 > kRingStageElems ? (sizeof(DecodeLds<D, G, kPfWaves>) + 1) / 2
+                                                                   : kRingStageElems;
+}
+
+template <int KVDT, int D, int G, bool RING>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_kernel(AttnArgs a, int queue0) {
-    __shared__ PrefillLds<D> lds;
-    prefill_queue<KVDT, D, G>(a, queue0 + blockIdx.x, lds);
+    if constexpr (RING) {
+        __shared__ __attribute__((aligned(16))) uint16_t s0[kRingStageElems], s1[kRingStageElems],
+            s2[kRingStageElems], s3[kRingStageElems];
+        prefill_queue_ring<G>(a, queue0 + blockIdx.x, s0, s1, s2, s3);
+    } else {
+        __shared__ PrefillLds<D> lds;
+        prefill_queue<KVDT, D, G>(a, queue0 + blockIdx.x, lds);
+    }
 }
 
 // Both halves of a mixed step in one launch: blocks below num_decode_queues
 // walk the decode queues with the decode unit, the others the prefill queues,
 // so that the bandwidth-bound decode rows and the matrix-core chunk tiles run
-// side by side on every CU (one 8-wave workgroup of each fits at <= 128
-// VGPRs).
+// side by side on every CU (two 8-wave workgroups fit at <= 128 VGPRs).
 template <int KVDT, int D, int G>
 constexpr size_t mixed_lds_bytes() {
     return sizeof(DecodeLds<D, G, kPfWaves>) > sizeof(PrefillLds<D>) ? sizeof(DecodeLds<D, G, kPfWaves>)
                                                                       : sizeof(PrefillLds<D>);
 }
 
-template <int KVDT, int D, int G>
+template <int D, int G>
+__device__ __forceinline__ void mixed_decode_queue(const AttnArgs& a, int b, DecodeLds<D, G, kPfWaves>& lds) {
+    const const_ptr<Unit> units = as_const(a.units);
+    const const_ptr<int32_t> qoff = as_const(a.queue_off);
+    const int u_end = qoff[b + 1];
+    for (int ui = qoff[b]; ui < u_end; ++ui)
+        decode_unit<PKV_DTYPE_BF16, PKV_DTYPE_BF16, D, G, kPfWaves, true>(a, load_unit(units, ui), lds);
+}
+
+template <int KVDT, int D, int G, bool RING>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void mixed_kernel(AttnArgs a, int num_decode_queues) {
-    __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<KVDT, D, G>()];
+    static_assert(KVDT == PKV_DTYPE_BF16, "one launch for bf16 K/V");
     const int b = blockIdx.x;
-    if (b < num_decode_queues) {
-        const const_ptr<Unit> units = as_const(a.units);
-        const const_ptr<int32_t> qoff = as_const(a.queue_off);
-        const int u_end = qoff[b + 1];
-        for (int ui = qoff[b]; ui < u_end; ++ui)
-            decode_unit<PKV_DTYPE_BF16, KVDT, D, G, kPfWaves, true>(
-                a, load_unit(units, ui), *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(smem));
+    if constexpr (RING) {
+        __shared__ __attribute__((aligned(16))) uint16_t s0[ring_stage0_elems<D, G>()], s1[kRingStageElems],
+            s2[kRingStageElems], s3[kRingStageElems];
+        if (b < num_decode_queues)
+            mixed_decode_queue<D, G>(a, b, *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(s0));
+        else
+            prefill_queue_ring<G>(a, b, s0, s1, s2, s3);
     } else {
-        prefill_queue<KVDT, D, G>(a, b, *reinterpret_cast<PrefillLds<D>*>(smem));
+        __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<KVDT, D, G>()];
+        if (b < num_decode_queues)
+            mixed_decode_queue<D, G>(a, b, *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(smem));
+        else
+            prefill_queue<KVDT, D, G>(a, b, *reinterpret_cast<PrefillLds<D>*>(smem));
     }
 }
 
+// The direct-to-LDS path serves bf16 K/V at D = 128 on power-of-two pages of
+// at least 16 tokens.
+template <int KVDT, int D>
+constexpr bool ring_capable() {
+    return KVDT == PKV_DTYPE_BF16 && D == 128;
+}
+__host__ inline bool ring_pages(const AttnArgs& a) { return a.block_shift >= 4; }
+
 template <int KVDT, int D, int G>
 int launch_prefill_t(const AttnArgs& a, int num_queues, int queue0, hipStream_t st) {
-    hipLaunchKernelGGL((prefill_kernel<KVDT, D, G>), dim3(num_queues), dim3(kPfWaves * 64), 0, st, a, queue0);
+    if constexpr (ring_capable<KVDT, D>()) {
+        if (ring_pages(a)) {
+            hipLaunchKernelGGL((prefill_kernel<KVDT, D, G, true>), dim3(num_queues), dim3(kPfWaves * 64), 0, st, a,
+                               queue0);
+            return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<KVDT, D, G, false>), dim3(num_queues), dim3(kPfWaves * 64), 0, st, a, queue0);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
@@ -429,14 +708,19 @@ template <int KVDT>
 int launch_mixed_d(const AttnArgs& a, int d, int group, int num_decode_queues, int num_prefill_queues,
                    hipStream_t st) {
     const dim3 grid(num_decode_queues + num_prefill_queues), block(kPfWaves * 64);
-    if (d == 128 && group == 4)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4>), grid, block, 0, st, a, num_decode_queues);
+    const bool ring = ring_pages(a);
+    if (d == 128 && group == 4 && ring)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, true>), grid, block, 0, st, a, num_decode_queues);
+    else if (d == 128 && group == 4)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, false>), grid, block, 0, st, a, num_decode_queues);
+    else if (d == 128 && group == 2 && ring)
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, true>), grid, block, 0, st, a, num_decode_queues);
     else if (d == 128 && group == 2)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, false>), grid, block, 0, st, a, num_decode_queues);
     else if (d == 64 && group == 4)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 4>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 4, false>), grid, block, 0, st, a, num_decode_queues);
     else if (d == 64 && group == 2)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 2>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 2, false>), grid, block, 0, st, a, num_decode_queues);
     else
         return PKV_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
