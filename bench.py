@@ -13,7 +13,9 @@ scattered-vs-contiguous comparison), ``fp8prefix`` (128 sequences over a
 shared 4096-token prefix, fp8 cache), ``mixed`` (63 decodes and one 512-row
 prefill chunk packed in one step; "nanoserve" chunked prefill) and
 ``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
-peak).
+peak).  ``--study skew`` and ``--study plan-cost`` print, instead of the bench
+line, one JSON line per case of the load-balance study (length mixes of equal
+total tokens at batch 4-128) and of the planner-cost sweep (batch 8-512).
 
 Inputs are synthetic: block tables, lengths and slots come from the seeded
 generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
@@ -215,6 +217,88 @@ def copy_calibration(torch):
           flush=True)
 
 
+def queue_balance(pkv, st, num_queues):
+    """Largest over mean decode-queue load of the host plan, in 16-key tiles."""
+    from paged_kv_attention_write_amd import _abi
+
+    p, image = _abi.plan_host(st["context_lens"], None, 32, 8, 128, num_queues)
+    units, qoff, _ = _abi.decode_plan_image(p, image)
+    ctx = st["context_lens"]
+    ends = np.minimum(units[:, 2], ctx[units[:, 0]])
+    tiles = np.maximum(0, -(-(ends - units[:, 1]) // 16))
+    loads = np.array([tiles[qoff[q]:qoff[q + 1]].sum() for q in range(int(p.num_queues))], dtype=np.float64)
+    return float(loads.max() / loads.mean()) if loads.mean() > 0 else 1.0
+
+
+def study_skew(args, torch, pkv, workloads, byte_model):
+    """Load-balance study: decode calls over length mixes of equal total
+    tokens (uniform, one long sequence holding half, Pareto-tailed) at batch
+    4 / 16 / 64 / 128, one JSON line per case."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    for batch in (4, 16, 64, 128):
+        for mix in workloads.SKEW_MIXES:
+            lens = workloads.skew_lengths(mix, batch)
+            st = workloads.structure_for_lengths(workloads.CONFIG_IDS["skew"], lens)
+            layers = build_layers(torch, st, {"config": "decode"}, args.layers, dev)
+            tables = torch.from_numpy(st["block_tables"]).to(dev)
+            ctx = torch.from_numpy(st["context_lens"]).to(dev)
+            plan = pkv.Plan(lens, None, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                            num_queues=args.queues)
+            n = args.steps * len(layers)
+            ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            plan_s = []
+            for it in range(args.warmup + args.steps):
+                plan.update(lens, None)
+                plan_s.append(plan.last_plan_s)
+                for l, layer in enumerate(layers):
+                    k = (it - args.warmup) * len(layers) + l
+                    if k >= 0:
+                        ev_a[k].record(stream)
+                    pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan)
+                    if k >= 0:
+                        ev_b[k].record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+            nbytes = byte_model.attention_bytes(lens, st["q_lens"], 32, 8, 128, st["block_size"], 2, 2)
+            p50 = float(np.median(ms)) * 1e-3
+            print(json.dumps({
+                "study": "skew", "mix": mix, "batch": batch, "total_tokens": int(lens.sum()),
+                "longest": int(lens.max()), "shortest": int(lens.min()),
+                "call_us": {"p10": round(float(np.percentile(ms, 10)) * 1e3, 2), "p50": round(p50 * 1e6, 2),
+                            "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+                "TBps": round(nbytes / p50 / 1e12, 4), "frac_of_8TBps": round(nbytes / p50 / 8e12, 4),
+                "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
+                         "merges": int(plan.desc.num_merges),
+                         "max_over_mean_queue_tiles": round(queue_balance(pkv, st, int(plan.desc.num_queues)), 4),
+                         "plan_us_per_step": round(float(np.median(plan_s)) * 1e6, 2)},
+                "layers": len(layers)}), flush=True)
+            del layers, plan
+            torch.cuda.empty_cache()
+
+
+def study_plan_cost(args, torch, pkv, workloads):
+    """Host planner cost per step (reused by all layers) for batch 8..512 with
+    context uniform in [512, 4096], one JSON line per batch."""
+    dev = torch.device("cuda:0")
+    for batch in (8, 16, 32, 64, 128, 256, 512):
+        lens = workloads.rng_for(workloads.CONFIG_IDS["skew"], 100 + batch).integers(
+            512, 4096, size=batch, endpoint=True).astype(np.int32)
+        plan = pkv.Plan(lens, None, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                        num_queues=args.queues)
+        ts = []
+        for _ in range(50):
+            plan.update(lens, None)
+            ts.append(plan.last_plan_s)
+        torch.cuda.synchronize()
+        med = float(np.median(ts[5:]))
+        print(json.dumps({"study": "plan-cost", "batch": batch, "plan_us_per_step": round(med * 1e6, 2),
+                          "plan_us_per_layer": round(med * 1e6 / LAYERS, 3), "units": int(plan.desc.num_units),
+                          "merges": int(plan.desc.num_merges)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +311,9 @@ def main():
     ap.add_argument("--queues", type=int, default=0, help="planner queues (0: the library default, 2 per CU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
+    ap.add_argument("--study", choices=["skew", "plan-cost"],
+                    help="instead of the bench line: the load-balance study over length mixes (skew) or the "
+                         "planner cost over batch sizes (plan-cost), one JSON line per case")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); sharding across GPUs is not built",
@@ -242,6 +329,13 @@ def main():
     import paged_kv_attention_write_amd as pkv
     import workloads
     from workloads import byte_model
+
+    if args.study == "skew":
+        study_skew(args, torch, pkv, workloads, byte_model)
+        return
+    if args.study == "plan-cost":
+        study_plan_cost(args, torch, pkv, workloads)
+        return
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")

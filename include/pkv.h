@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 /* Status codes. */
 #define PKV_OK 0
@@ -105,6 +105,9 @@ typedef struct pkv_plan {
     int32_t max_q_len;
     int32_t num_prefill_queues; /* workgroups of the prefill launch (0: no chunk rows) */
     int32_t num_prefill_units;  /* of num_units; they sit after the decode units */
+    int32_t num_wide_merges;  /* merge records listed first: one row each whose pieces are
+                                 many (merged by several waves per q head) */
+    int32_t reserved0;
     int64_t off_units;        /* byte offsets inside the workspace */
     int64_t off_queues;
     int64_t off_merges;
@@ -114,7 +117,7 @@ typedef struct pkv_plan {
     int64_t workspace_bytes;  /* bytes of workspace the plan uses */
 } pkv_plan;
 
-#define PKV_PLAN_MAGIC 0x504b5632 /* "PKV2" */
+#define PKV_PLAN_MAGIC 0x504b5633 /* "PKV3" */
 
 /* Text of a status code; never NULL. */
 const char* paged_attn_strerror(int status);

@@ -64,6 +64,8 @@ class PkvPlan(ctypes.Structure):
         ("max_q_len", ctypes.c_int32),
         ("num_prefill_queues", ctypes.c_int32),
         ("num_prefill_units", ctypes.c_int32),
+        ("num_wide_merges", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
         ("off_units", ctypes.c_int64),
         ("off_queues", ctypes.c_int64),
         ("off_merges", ctypes.c_int64),

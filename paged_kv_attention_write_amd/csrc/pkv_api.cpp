@@ -53,7 +53,8 @@ int check_attention(void* out, const void* q, int32_t q_dtype, int64_t q_token_s
         (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f))
         return PKV_ERR_SHAPE;
     if (plan->magic != PKV_PLAN_MAGIC || plan->num_seqs != num_seqs || plan->num_tokens != rows ||
-        plan->num_q_heads != hq || plan->num_kv_heads != hkv || plan->head_dim != d)
+        plan->num_q_heads != hq || plan->num_kv_heads != hkv || plan->head_dim != d ||
+        plan->num_wide_merges < 0 || plan->num_wide_merges > plan->num_merges)
         return PKV_ERR_PLAN;
     if (rows == 0) return PKV_OK;
     if (out == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
@@ -223,7 +224,7 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
     st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
     if (st != PKV_OK) return st;
     const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, 1, q_dtype, head_dim, stream);
+    return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, 1, q_dtype, head_dim, stream);
 }
 
 // Most rows of any merge record: decode merges have one, prefill merges a row block.
@@ -259,7 +260,8 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
         st = launch_mixed(a, head_dim, group, plan->num_queues, plan->num_prefill_queues, stream);
         if (st != PKV_OK) return st;
         const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-        return launch_merge(a, merges, plan->num_merges, merge_rows(plan, group), q_dtype, head_dim, stream);
+        return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, merge_rows(plan, group), q_dtype,
+                            head_dim, stream);
     }
     if (plan->num_units > plan->num_prefill_units) {
         st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
@@ -271,7 +273,8 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
         if (st != PKV_OK) return st;
     }
     const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, merge_rows(plan, group), q_dtype, head_dim, stream);
+    return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, merge_rows(plan, group), q_dtype,
+                            head_dim, stream);
 }
 
 }  // extern "C"

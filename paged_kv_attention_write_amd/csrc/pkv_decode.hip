@@ -31,64 +31,70 @@ void decode_kernel(AttnArgs a) {
 constexpr int kMergeWaves = 4;
 constexpr int kMergeBatch = 8;
 
-template <int QDT, int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __restrict__ merges,
-                                                                 const float* __restrict__ po,
-                                                                 const float* __restrict__ pl,
-                                                                 void* __restrict__ out, int hq, float v_scale) {
-    constexpr int E = D / 64;  // elements per lane
-    constexpr int B = kMergeBatch;
-    const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + blockIdx.x);
-    const int row0 = mw[0], nrows = mw[1], prow0 = mw[2], parts = mw[3];
-    const int r = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int h = blockIdx.z * kMergeWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (h >= hq || r >= nrows) return;
-    const int64_t hd = static_cast<int64_t>(hq) * D;
-    const const_ptr<float> lse = as_const(pl);
-    float M = -INFINITY;  // running maximum of the lse values seen
-    float sw = 0.f;       // sum of 2^(lse - M)
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+// Running merge state of one wave over some parts of one (row, q head): the
+// largest LSE seen, the sum of 2^(lse - M), and the lane's D/64 elements of
+// the weighted sum of the parts' normalised outputs.
+template <int E>
+struct MergeState {
+    float M = -INFINITY;
+    float sw = 0.f;
+    float acc[E] = {};
     bool nan = false;
-    for (int c0 = 0; c0 < parts; c0 += B) {
+};
+
+// Fold parts c0, c0 + step, ... (< parts) of row r, q head h into st,
+// kMergeBatch parts per round trip: every part's LSE and its elements are
+// loaded before any is used.  A NaN LSE (a bad block id in some piece) makes
+// the row NaN; empty parts (lse = -inf) drop out.
+template <int D>
+__device__ __forceinline__ void merge_fold(MergeState<D / 64>& st, const float* __restrict__ po,
+                                           const_ptr<float> lse, int hq, int prow0, int nrows, int parts, int r, int h,
+                                           int c0, int step, int lane) {
+    constexpr int E = D / 64;
+    constexpr int B = kMergeBatch;
+    const int64_t hd = static_cast<int64_t>(hq) * D;
+    for (int cb = c0; cb < parts; cb += B * step) {
         float l[B];
         float x[B][E];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            const int64_t prow = prow0 + static_cast<int64_t>(min(c0 + b, parts - 1)) * nrows + r;
+            const int64_t prow = prow0 + static_cast<int64_t>(min(cb + b * step, parts - 1)) * nrows + r;
             l[b] = lse[prow * hq + h];
             const float* src = po + prow * hd + static_cast<int64_t>(h) * D + lane * E;
 #pragma unroll
             for (int e = 0; e < E; ++e) x[b][e] = src[e];
         }
-        float mb = M;
+        float mb = st.M;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            if (c0 + b >= parts) l[b] = -INFINITY;  // a repeated last part counts once
-            nan |= l[b] != l[b];
+            if (cb + b * step >= parts) l[b] = -INFINITY;  // a repeated last part counts once
+            st.nan |= l[b] != l[b];
             mb = fmaxf(mb, l[b]);
         }
         if (mb == -INFINITY) continue;  // every part so far is empty
-        const float f = exp2_fast(M - mb);  // 0 while M is -inf
-        sw *= f;
+        const float f = exp2_fast(st.M - mb);  // 0 while M is -inf
+        st.sw *= f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] *= f;
+        for (int e = 0; e < E; ++e) st.acc[e] *= f;
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const float w = exp2_fast(l[b] - mb);  // 0 for an empty part
-            sw += w;
+            st.sw += w;
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[b][e], acc[e]);
+            for (int e = 0; e < E; ++e) st.acc[e] = fmaf(w, x[b][e], st.acc[e]);
         }
-        M = mb;
+        st.M = mb;
     }
+}
+
+template <int QDT, int D>
+__device__ __forceinline__ void merge_store(void* __restrict__ out, int64_t oi, const float (&acc)[D / 64], float sw,
+                                            bool nan, float v_scale) {
+    constexpr int E = D / 64;
     const float scale = sw > 0.f ? v_scale / sw : 0.f;
     float o[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) o[e] = nan ? NAN : acc[e] * scale;
-    const int64_t oi = static_cast<int64_t>(row0 + r) * hd + static_cast<int64_t>(h) * D + lane * E;
     if constexpr (QDT == PKV_DTYPE_F32) {
 #pragma unroll
         for (int e = 0; e < E; ++e) static_cast<float*>(out)[oi + e] = o[e];
@@ -96,6 +102,79 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
 #pragma unroll
         for (int e = 0; e < E; ++e) static_cast<uint16_t*>(out)[oi + e] = static_cast<uint16_t>(f32_to_bf16_rne(o[e]));
     }
+}
+
+// One launch over all merge records (a 1-D grid of kMergeWaves-wave
+// workgroups).  The plan lists its wide records first (one row, at least
+// kWideMergeParts pieces): blocks [0, num_wide * hq) give each (wide record,
+// q head) a workgroup whose wave w folds parts w, w + kMergeWaves, ..., the
+// waves' states then combining through LDS (each scaled by 2^(m_w - M), an
+// empty wave contributing nothing).  The remaining blocks give each (record,
+// row, group of kMergeWaves q heads) a workgroup, one wave per head folding
+// all of its parts.
+template <int QDT, int D>
+__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __restrict__ merges,
+                                                                 const float* __restrict__ po,
+                                                                 const float* __restrict__ pl,
+                                                                 void* __restrict__ out, int hq, float v_scale,
+                                                                 int num_wide, int max_rows) {
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t hd = static_cast<int64_t>(hq) * D;
+    const const_ptr<float> lse = as_const(pl);
+    const int b = blockIdx.x;
+    const int wide_blocks = num_wide * hq;
+    if (b < wide_blocks) {
+        __shared__ float sh_m[kMergeWaves], sh_s[kMergeWaves];
+        __shared__ int sh_nan[kMergeWaves];
+        __shared__ float sh_acc[kMergeWaves][D];
+        const int rec = b / hq, h = b % hq;
+        const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + rec);
+        const int row0 = mw[0], prow0 = mw[2], parts = mw[3];
+        MergeState<E> st;
+        merge_fold<D>(st, po, lse, hq, prow0, 1, parts, 0, h, wave, kMergeWaves, lane);
+        if (lane == 0) {
+            sh_m[wave] = st.M;
+            sh_s[wave] = st.sw;
+            sh_nan[wave] = st.nan ? 1 : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) sh_acc[wave][lane * E + e] = st.acc[e];
+        __syncthreads();
+        if (wave != 0) return;
+        float Mt = -INFINITY;
+        bool nan = false;
+#pragma unroll
+        for (int w = 0; w < kMergeWaves; ++w) {
+            Mt = fmaxf(Mt, sh_m[w]);
+            nan |= sh_nan[w] != 0;
+        }
+        float sw = 0.f;
+        float acc[E] = {};
+#pragma unroll
+        for (int w = 0; w < kMergeWaves; ++w) {
+            const float f = sh_m[w] == -INFINITY ? 0.f : exp2_fast(sh_m[w] - Mt);
+            sw = fmaf(f, sh_s[w], sw);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] = fmaf(f, sh_acc[w][lane * E + e], acc[e]);
+        }
+        merge_store<QDT, D>(out, static_cast<int64_t>(row0) * hd + static_cast<int64_t>(h) * D + lane * E, acc, sw,
+                            nan, v_scale);
+        return;
+    }
+    const int hgroups = (hq + kMergeWaves - 1) / kMergeWaves;
+    const int b2 = b - wide_blocks;
+    const int rec = num_wide + b2 / (max_rows * hgroups);
+    const int r = (b2 / hgroups) % max_rows;
+    const int h = (b2 % hgroups) * kMergeWaves + wave;
+    const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + rec);
+    const int row0 = mw[0], nrows = mw[1], prow0 = mw[2], parts = mw[3];
+    if (h >= hq || r >= nrows) return;
+    MergeState<E> st;
+    merge_fold<D>(st, po, lse, hq, prow0, nrows, parts, r, h, 0, 1, lane);
+    merge_store<QDT, D>(out, static_cast<int64_t>(row0 + r) * hd + static_cast<int64_t>(h) * D + lane * E, st.acc,
+                        st.sw, st.nan, v_scale);
 }
 
 // Launch shape: one persistent workgroup per queue.  8 waves (one per kv head
@@ -165,24 +244,28 @@ int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, in
     return PKV_ERR_UNSUPPORTED;
 }
 
-int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int max_rows, int q_dtype, int head_dim,
-                 void* stream) {
+int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int num_wide, int max_rows, int q_dtype,
+                 int head_dim, void* stream) {
     if (num_merges == 0) return PKV_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(num_merges, max_rows, (a.hq + kMergeWaves - 1) / kMergeWaves);
+    const int64_t hgroups = (a.hq + kMergeWaves - 1) / kMergeWaves;
+    const int64_t blocks = static_cast<int64_t>(num_wide) * a.hq +
+                           static_cast<int64_t>(num_merges - num_wide) * max_rows * hgroups;
+    if (blocks > 0x7FFFFFFF) return PKV_ERR_SHAPE;
+    const dim3 grid(static_cast<uint32_t>(blocks));
     const dim3 block(kMergeWaves * 64);
     if (q_dtype == PKV_DTYPE_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_F32, 64>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale);
+                           a.out, a.hq, a.v_scale, num_wide, max_rows);
     else if (q_dtype == PKV_DTYPE_F32)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_F32, 128>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale);
+                           a.out, a.hq, a.v_scale, num_wide, max_rows);
     else if (head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_BF16, 64>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale);
+                           a.out, a.hq, a.v_scale, num_wide, max_rows);
     else
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_BF16, 128>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale);
+                           a.out, a.hq, a.v_scale, num_wide, max_rows);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -30,6 +30,10 @@ constexpr int kPrefillQueuesPerQueue = 2;
 constexpr int64_t kFlopsPerTile = 13000000;
 
 // Alignment of the sections of the workspace.
+// A one-row merge record with at least this many pieces is "wide": its
+// merge gives every q head a workgroup whose waves split the pieces.
+constexpr int kWideMergeParts = 4;
+
 constexpr size_t kAlign = 256;
 
 // kind == kUnitDecode: a decode unit (one row, every kv head).  kind >= 1: a

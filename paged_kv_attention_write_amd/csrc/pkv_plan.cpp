@@ -204,6 +204,12 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         }
     }
 
+    // wide merge records (one row, many pieces) first, each group in its order
+    std::stable_partition(merges.begin(), merges.end(),
+                          [](const Merge& m) { return m.nrows == 1 && m.parts >= kWideMergeParts; });
+    int32_t num_wide = 0;
+    for (const auto& m : merges) num_wide += (m.nrows == 1 && m.parts >= kWideMergeParts) ? 1 : 0;
+
     int64_t num_units = 0;
     for (const auto& q : queues) num_units += static_cast<int64_t>(q.size());
     const int64_t num_prefill_units = static_cast<int64_t>(prefill.size());
@@ -235,6 +241,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     plan->max_q_len = max_q;
     plan->num_prefill_queues = prefill_queues;
     plan->num_prefill_units = static_cast<int32_t>(num_prefill_units);
+    plan->num_wide_merges = num_wide;
+    plan->reserved0 = 0;
     plan->off_units = 0;
     plan->off_queues = static_cast<int64_t>(units_bytes);
     plan->off_merges = static_cast<int64_t>(units_bytes + queues_bytes);

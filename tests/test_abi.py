@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.pkv_abi_version() == 2
+    assert L.pkv_abi_version() == 3
 
 
 def test_strerror_covers_all_codes():
@@ -89,6 +89,25 @@ def test_plan_partials_and_merges_are_consistent():
     whole = units[units[:, 6] < 0]
     assert not split & set(whole[:, 0].tolist())
     assert p.workspace_bytes >= p.off_partial_lse + 4 * 32 * p.num_partial_rows
+    _check_wide_first(p, merges)
+
+
+def _check_wide_first(p, merges):
+    """Wide merge records (one row, at least 4 pieces) are listed first and counted."""
+    wide = (merges[:, 1] == 1) & (merges[:, 3] >= 4)
+    nw = int(p.num_wide_merges)
+    assert nw == int(wide.sum()) and bool(np.all(wide[:nw])) and not bool(np.any(wide[nw:]))
+
+
+@pytest.mark.parametrize("mix", ["uniform", "one-long", "heavy"])
+@pytest.mark.parametrize("batch", [4, 64, 128])
+def test_wide_merges_first_on_skew_mixes(mix, batch):
+    import workloads
+
+    lens = workloads.skew_lengths(mix, batch)
+    p, image = pkv.plan_host(lens, None, 32, 8, 128, 256)
+    _, _, merges = pkv.decode_plan_image(p, image)
+    _check_wide_first(p, merges)
 
 
 def _mixed_case():
@@ -123,6 +142,7 @@ def test_mixed_plan_covers_every_visible_pair_once():
                     cover[max(kind - 1, 0), r + i, lo:hi] += 1
         visible = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]
         assert np.array_equal(cover, np.broadcast_to(visible.astype(np.int32), cover.shape)), s
+    _check_wide_first(p, merges)
     # every merged block lists its pieces at prow0 + c * nrows
     for row0, nrows, prow0, parts in merges:
         us = units[(units[:, 3] == row0) & (units[:, 6] >= 0)]

@@ -211,3 +211,41 @@ def test_plan_reused_across_layers(gpu):
         kr, vr = oracle_caches(case)
         ref, _ = oracle_attention(case, kr, vr)
         check_close(got, ref, "bf16", f"layer {layer}")
+
+
+@pytest.mark.parametrize("mix", workloads.SKEW_MIXES)
+@pytest.mark.parametrize("batch", [4, 16, 64])
+def test_skew_mixes(gpu, mix, batch):
+    """The load-balance study's length mixes (equal total tokens: uniform, one
+    sequence holding half, Pareto-tailed) at a reduced total of 24576 tokens;
+    default queues split the long sequences into many pieces."""
+    log(f"skew {mix} batch={batch}")
+    lens = workloads.skew_lengths(mix, batch, total=24576)
+    case = workloads.build_case(f"skew-{mix}-{batch}", 60 + batch, lens, [1] * batch, num_q_heads=32,
+                                num_kv_heads=8, head_dim=128, block_size=16)
+    got, ref, plan, _ = _run(case, gpu)
+    check_close(got, ref, "bf16", f"skew {mix} B={batch} units={plan.desc.num_units} merges={plan.desc.num_merges}")
+
+
+def test_invalid_block_id_in_a_wide_merge(gpu):
+    """A long sequence cut into many pieces (a wide merge record, its parts
+    split over several waves per head) with one table entry outside the pool:
+    its row comes out NaN, the short neighbours are unaffected."""
+    import paged_kv_attention_write_amd as pkv
+
+    case = workloads.build_case("badwide", 62, [40, 3000, 70], [1, 1, 1], num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, block_size=16)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    plan = dc.plan(24)
+    assert plan.desc.num_wide_merges >= 1
+    out = as_f64(dc.decode(plan))
+    check_close(out, ref, "bf16", f"wide merge wide={plan.desc.num_wide_merges}")
+    tables = case.block_tables.copy()
+    tables[1, 100] = case.num_blocks + 7
+    dc.tables = to_dev(tables, gpu)
+    out = as_f64(dc.decode(plan))
+    assert np.all(np.isnan(out[1]))
+    check_close(out[[0, 2]], ref[[0, 2]], "bf16", "neighbours of the bad wide row")

@@ -21,6 +21,11 @@ Shapes follow the pages' workloads:
   (a 4096-token shared prefix) plus 256 private tokens each, fp8 E4M3 cache
   filled from bf16 N(0,1) values with one scale per tensor.
 
+* ``skew``      - length mixes at an equal total of tokens for the load-balance
+  study (batch 4/16/64/128): ``uniform`` (all equal), ``one-long`` (one
+  sequence holds half the tokens, the others share the rest) and ``heavy``
+  (Pareto(1.2)-tailed draws scaled to the total), same heads and page 16.
+
 Random streams: ``numpy.random.default_rng([config_id, stream])`` with stream
 0 = lengths, 1 = pool permutation, 2 = K pool, 3 = V pool, 4 = Q, 5 = new K,
 6 = new V.  Values are N(0, 1) in fp32, rounded to the storage dtype (bf16 by
@@ -43,7 +48,7 @@ from typing import Optional
 
 import numpy as np
 
-CONFIG_IDS = {"tiny": 0, "decode": 1, "long": 2, "mixed": 3, "fp8prefix": 4}
+CONFIG_IDS = {"tiny": 0, "decode": 1, "long": 2, "mixed": 3, "fp8prefix": 4, "skew": 5}
 
 STORAGE_NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 STORAGE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -297,6 +302,50 @@ def make_case(config: str, layout: str = "page16") -> Case:
                           num_kv_heads=8, head_dim=128, block_size=16, kv_dtype="fp8",
                           new_dtype="bf16", shared_prefix_tokens=4096)
     raise ValueError(config)
+
+
+SKEW_MIXES = ("uniform", "one-long", "heavy")
+SKEW_TOTAL = 64 * 2304  # the decode workload's expected total of context tokens
+
+
+def skew_lengths(mix: str, batch: int, total: int = SKEW_TOTAL, min_len: int = 16) -> np.ndarray:
+    """Context lengths of one skew case: ``batch`` sequences summing to
+    ``total`` tokens (each at least ``min_len``)."""
+    if batch < 1 or total < batch * min_len:
+        raise ValueError("batch and total do not fit")
+    if mix == "uniform":
+        w = np.ones(batch)
+    elif mix == "one-long":
+        w = np.ones(batch) if batch == 1 else np.concatenate([[batch - 1.0], np.ones(batch - 1)])
+    elif mix == "heavy":
+        w = 1.0 + rng_for(CONFIG_IDS["skew"], 0 + 16 * batch).pareto(1.2, size=batch)
+    else:
+        raise ValueError(mix)
+    spare = total - batch * min_len
+    lens = min_len + np.floor(spare * w / w.sum()).astype(np.int64)
+    lens[np.argmax(w)] += total - int(lens.sum())  # the rounding remainder goes to the longest
+    return lens.astype(np.int32)
+
+
+def structure_for_lengths(config_id: int, context_lens, q_lens=None, block_size: int = 16, layout: str = "shuffle"):
+    """Tables, slots and offsets for given lengths (the pool holds exactly the
+    sequences' blocks, in seeded random order or in order), no values."""
+    lens = np.asarray(context_lens, dtype=np.int32)
+    ql = np.ones(lens.shape[0], np.int32) if q_lens is None else np.asarray(q_lens, dtype=np.int32)
+    bs = int(block_size)
+    counts = [int(-(-int(n) // bs)) for n in lens]
+    nblocks = max(1, sum(counts))
+    perm = rng_for(config_id, 1).permutation(nblocks) if layout == "shuffle" else np.arange(nblocks)
+    tables = _tables(counts, 0, nblocks, perm.astype(np.int32))
+    slots = []
+    for s in range(lens.shape[0]):
+        n, L = int(lens[s]), int(ql[s])
+        pos = np.arange(n - L, n)
+        slots.append(tables[s, pos // bs].astype(np.int64) * bs + pos % bs)
+    cu = np.zeros(lens.shape[0] + 1, np.int32)
+    cu[1:] = np.cumsum(ql)
+    return dict(context_lens=lens, q_lens=ql, cu_seqlens=cu, block_tables=tables,
+                slot_mapping=np.concatenate(slots).astype(np.int32), num_blocks=nblocks, block_size=bs)
 
 
 def structure_only(config: str, layout: str = "page16"):
