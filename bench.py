@@ -24,7 +24,13 @@ library's own write).  They are resident in HBM before timing starts.
 
 Printed: one JSON line.  ``value`` is the step's algorithmic bytes (every
 valid K/V element, q, out, table entries, lengths, and the write's bytes) over
-its wall time, in TB/s.  ``roofline`` covers the dominant call (the attention
+its wall time, in TB/s.  The step is timed twice: as eager launches (with HIP
+events around every attention call, which feed ``roofline``) and, unless
+``--no-graph``, as one captured HIP graph of all the layers' writes and
+attention calls, replayed after each step's re-plan into a fixed-capacity
+workspace; ``value`` and ``ms_per_step`` come from the replays then (both
+step times are in ``graph``), and layer 0's output of the last replay is
+the one checked against the oracle.  ``roofline`` covers the dominant call (the attention
 call: its kernel and the merge kernel), timed with HIP events around every
 call on its stream; with prefill chunks in the step it reads the chunk's
 flops against the bf16 matrix-core peak when that fraction is the larger.
@@ -311,6 +317,10 @@ def main():
     ap.add_argument("--queues", type=int, default=0, help="planner queues (0: the library default, 2 per CU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="time the step only as eager launches (by default the step is also captured once as a "
+                         "HIP graph of every layer's write + attention, the plan made for a fixed capacity, and "
+                         "replayed after each step's re-plan; value and ms_per_step then come from the replays)")
     ap.add_argument("--study", choices=["skew", "plan-cost"],
                     help="instead of the bench line: the load-balance study over length mixes (skew) or the "
                          "planner cost over batch sizes (plan-cost), one JSON line per case")
@@ -413,6 +423,50 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     decode_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    eager_ms_step = wall * 1e3 / args.steps
+    graph_info = None
+    if args.graph:
+        # the same step captured once (writes and attention calls of every
+        # layer) with a plan of fixed capacity; each timed step re-plans into
+        # that plan's workspace, then replays it
+        plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                        num_queues=args.queues, capacity=(B, T))
+
+        def layers_only():
+            for l, layer in enumerate(layers):
+                ks, vs = scales[l]
+                pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
+                if mixed:
+                    pkv.paged_attn_mixed(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, cu, ctx, scale,
+                                         plan, ks, vs)
+                else:
+                    pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale,
+                                          plan, ks, vs)
+
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layers_only()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layers_only()
+        torch.cuda.synchronize()
+        log("graph timed")
+        for _ in range(args.warmup):
+            plan.update(st["context_lens"], q_lens)
+            graph.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            plan.update(st["context_lens"], q_lens)
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - g0
+        graph_info = {"ms_per_step_graph": round(wall * 1e3 / args.steps, 4),
+                      "ms_per_step_eager": round(eager_ms_step, 4),
+                      "captured_per_step": f"{args.layers} x (paged_kv_write + attention call)"}
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e12
     call_s = float(decode_ms.mean()) / 1e3
@@ -467,6 +521,8 @@ def main():
         "plan": {"queues": int(plan.desc.num_queues), "units": int(plan.desc.num_units),
                  "merges": int(plan.desc.num_merges), "target_tiles": int(plan.desc.target_tiles)},
     }
+    if graph_info is not None:
+        result["graph"] = graph_info
     rec = recorded_traffic(args.config)
     if rec is not None:
         result["roofline"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])

@@ -107,6 +107,13 @@ typedef struct pkv_plan {
     int32_t num_prefill_units;  /* of num_units; they sit after the decode units */
     int32_t num_wide_merges;  /* merge records listed first: one row each whose pieces are
                                  many (merged by several waves per q head) */
+    int32_t num_block_merges; /* records listed next: blocks of chunk rows; the one-row
+                                 records with few pieces follow */
+    int32_t max_row_merges;   /* most one-row records any plan with these q_lens can have
+                                 (the rows with q_len 1) */
+    int32_t max_block_merges; /* most row-block records any plan with these q_lens can have;
+                                 these two size the merge launch of a call made while its
+                                 stream is being captured */
     int32_t reserved0;
     int64_t off_units;        /* byte offsets inside the workspace */
     int64_t off_queues;
@@ -211,6 +218,28 @@ int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
                     void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
                     pkv_plan* plan, void* stream);
+
+/*
+ * paged_attn_plan_capacity - paged_attn_plan with the image laid out for a
+ * capacity: units, queue offsets, merge records and partial results sit at
+ * the workspace offsets of any plan over at most max_seqs sequences and
+ * max_tokens query rows (the sizes paged_attn_workspace_size bounds), so
+ * every plan made with the same capacity, queues, heads and head_dim uses
+ * the same offsets and sizes.  Calls of paged_attn_decode / paged_attn_mixed
+ * captured once into a HIP graph with such a plan then stay valid for later
+ * plans of the same capacity and the same q_lens made into the same
+ * workspace (with the lengths, tables and pools updated in place): the
+ * lengths reach the kernels through the workspace, and a merge launch made
+ * while its stream is being captured is sized for max_row_merges and
+ * max_block_merges records and reads the live counts from the workspace.  The upload copies the whole
+ * image (image_bytes) each time.
+ * Errors as paged_attn_plan, plus PKV_ERR_SHAPE when num_seqs > max_seqs or
+ * the query rows exceed max_tokens.
+ */
+int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                             int32_t max_seqs, int32_t max_tokens, void* host_staging, size_t host_staging_bytes,
+                             void* workspace, size_t workspace_bytes, pkv_plan* plan, void* stream);
 
 /*
  * paged_attn_decode - one query row per sequence (token s is sequence s).

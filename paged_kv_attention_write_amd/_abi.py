@@ -43,6 +43,7 @@ EXPORTS = (
     "paged_attn_default_queues",
     "paged_attn_plan_host",
     "paged_attn_plan",
+    "paged_attn_plan_capacity",
     "paged_attn_decode",
     "paged_attn_mixed",
 )
@@ -65,6 +66,9 @@ class PkvPlan(ctypes.Structure):
         ("num_prefill_queues", ctypes.c_int32),
         ("num_prefill_units", ctypes.c_int32),
         ("num_wide_merges", ctypes.c_int32),
+        ("num_block_merges", ctypes.c_int32),
+        ("max_row_merges", ctypes.c_int32),
+        ("max_block_merges", ctypes.c_int32),
         ("reserved0", ctypes.c_int32),
         ("off_units", ctypes.c_int64),
         ("off_queues", ctypes.c_int64),
@@ -108,6 +112,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_plan_host.restype = ctypes.c_int
         L.paged_attn_plan.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, sz, vp, sz, P(PkvPlan), vp]
         L.paged_attn_plan.restype = ctypes.c_int
+        L.paged_attn_plan_capacity.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, sz,
+                                               P(PkvPlan), vp]
+        L.paged_attn_plan_capacity.restype = ctypes.c_int
         L.paged_attn_decode.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i64, i32,
                                         f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_decode.restype = ctypes.c_int
@@ -237,10 +244,16 @@ class Plan:
     ``last_plan_s`` is the host time of the last planner call (plan and
     upload issue) and ``last_wait_s`` the time spent waiting for a staging
     buffer to come free before it.
+
+    ``capacity=(max_seqs, max_tokens)`` makes every plan of this object use
+    ``paged_attn_plan_capacity``: buffers sized for the capacity are allocated
+    once and never replaced, and the image keeps the same offsets, so attention
+    calls captured into a HIP graph (e.g. ``torch.cuda.CUDAGraph``) stay valid
+    across updates with the same q_lens.
     """
 
     def __init__(self, context_lens, q_lens=None, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                 device=None, num_queues: int = 0, stream=None):
+                 device=None, num_queues: int = 0, stream=None, capacity=None):
         torch = _torch()
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
@@ -251,6 +264,17 @@ class Plan:
         self._turn = 0
         self.workspace = None
         self.desc = PkvPlan()
+        self.capacity = None
+        if capacity is not None:
+            max_seqs, max_tokens = (int(x) for x in capacity)
+            ws_b, host_b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+            _check(lib().paged_attn_workspace_size(max_seqs, max_tokens, num_q_heads, head_dim, self.num_queues,
+                                                   ctypes.byref(ws_b), ctypes.byref(host_b)),
+                   "paged_attn_workspace_size")
+            self._staging = [torch.empty(max(int(host_b.value), 256), dtype=torch.uint8, pin_memory=True)
+                             for _ in range(2)]
+            self.workspace = torch.empty(max(int(ws_b.value), 256), dtype=torch.uint8, device=self.device)
+            self.capacity = (max_seqs, max_tokens)
         self.update(context_lens, q_lens, stream=stream)
 
     def update(self, context_lens, q_lens=None, stream=None) -> "Plan":
@@ -269,14 +293,21 @@ class Plan:
             for attempt in range(2):
                 staging, ws = self._staging[i], self.workspace
                 t1 = time.perf_counter()
-                st = lib().paged_attn_plan(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads, self.num_kv_heads,
-                                           self.head_dim, self.num_queues,
-                                           staging.data_ptr() if staging is not None else None,
-                                           staging.numel() if staging is not None else 0,
-                                           ws.data_ptr() if ws is not None else None,
-                                           ws.numel() if ws is not None else 0, ctypes.byref(self.desc), st_ptr)
+                if self.capacity is not None:
+                    st = lib().paged_attn_plan_capacity(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                                        self.num_kv_heads, self.head_dim, self.num_queues,
+                                                        self.capacity[0], self.capacity[1], staging.data_ptr(),
+                                                        staging.numel(), ws.data_ptr(), ws.numel(),
+                                                        ctypes.byref(self.desc), st_ptr)
+                else:
+                    st = lib().paged_attn_plan(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                               self.num_kv_heads, self.head_dim, self.num_queues,
+                                               staging.data_ptr() if staging is not None else None,
+                                               staging.numel() if staging is not None else 0,
+                                               ws.data_ptr() if ws is not None else None,
+                                               ws.numel() if ws is not None else 0, ctypes.byref(self.desc), st_ptr)
                 self.last_plan_s = time.perf_counter() - t1
-                if st in (PKV_ERR_WORKSPACE, PKV_ERR_NULL) and attempt == 0:
+                if st in (PKV_ERR_WORKSPACE, PKV_ERR_NULL) and attempt == 0 and self.capacity is None:
                     probe = PkvPlan()
                     _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
                                                       self.num_kv_heads, self.head_dim, self.num_queues, None, 0,

@@ -54,7 +54,10 @@ int check_attention(void* out, const void* q, int32_t q_dtype, int64_t q_token_s
         return PKV_ERR_SHAPE;
     if (plan->magic != PKV_PLAN_MAGIC || plan->num_seqs != num_seqs || plan->num_tokens != rows ||
         plan->num_q_heads != hq || plan->num_kv_heads != hkv || plan->head_dim != d ||
-        plan->num_wide_merges < 0 || plan->num_wide_merges > plan->num_merges)
+        plan->num_wide_merges < 0 || plan->num_block_merges < 0 ||
+        plan->num_wide_merges + plan->num_block_merges > plan->num_merges ||
+        plan->num_wide_merges > plan->max_row_merges || plan->num_block_merges > plan->max_block_merges ||
+        plan->num_merges - plan->num_block_merges > plan->max_row_merges)
         return PKV_ERR_PLAN;
     if (rows == 0) return PKV_OK;
     if (out == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
@@ -205,6 +208,31 @@ int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host
     return PKV_OK;
 }
 
+int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                             int32_t max_seqs, int32_t max_tokens, void* host_staging, size_t host_staging_bytes,
+                             void* workspace, size_t workspace_bytes, pkv_plan* plan, void* stream) {
+    if (plan == nullptr || host_staging == nullptr || workspace == nullptr) return PKV_ERR_NULL;
+    if (max_seqs < 0 || max_tokens < 0) return PKV_ERR_SHAPE;
+    if (num_queues <= 0) {
+        const int st = paged_attn_default_queues(&num_queues);
+        if (st != PKV_OK) return st;
+    }
+    int st = plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
+                       host_staging, host_staging_bytes, plan, max_seqs, max_tokens);
+    if (st != PKV_OK) return st;
+    if (workspace_bytes < static_cast<size_t>(plan->workspace_bytes) || !aligned(workspace, kAlign)) {
+        plan->magic = 0;
+        return PKV_ERR_WORKSPACE;
+    }
+    if (hipMemcpyAsync(workspace, host_staging, static_cast<size_t>(plan->image_bytes), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(stream)) != hipSuccess) {
+        plan->magic = 0;
+        return PKV_ERR_HIP;
+    }
+    return PKV_OK;
+}
+
 int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
                       const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
@@ -223,8 +251,7 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
                                  scale, k_scale, v_scale, plan, workspace);
     st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
     if (st != PKV_OK) return st;
-    const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, 1, q_dtype, head_dim, stream);
+    return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
 }
 
 // Most rows of any merge record: decode merges have one, prefill merges a row block.
@@ -259,9 +286,7 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
     if (chunks && mixed_one_launch(q_dtype, kv_dtype, head_dim, group, block_size)) {
         st = launch_mixed(a, head_dim, group, plan->num_queues, plan->num_prefill_queues, stream);
         if (st != PKV_OK) return st;
-        const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-        return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, merge_rows(plan, group), q_dtype,
-                            head_dim, stream);
+        return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }
     if (plan->num_units > plan->num_prefill_units) {
         st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
@@ -272,9 +297,7 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
                             stream);
         if (st != PKV_OK) return st;
     }
-    const Merge* merges = reinterpret_cast<const Merge*>(static_cast<char*>(workspace) + plan->off_merges);
-    return launch_merge(a, merges, plan->num_merges, plan->num_wide_merges, merge_rows(plan, group), q_dtype,
-                            head_dim, stream);
+    return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
 }
 
 }  // extern "C"

@@ -70,7 +70,7 @@ bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int bl
 int launch_mixed(const AttnArgs& a, int head_dim, int group, int num_decode_queues, int num_prefill_queues,
                  void* stream);
 // max_rows: the most rows of any merge record (1 for a decode-only plan).
-int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int num_wide, int max_rows, int q_dtype,
+int launch_merge(const AttnArgs& a, const pkv_plan* plan, const void* workspace, int max_rows, int q_dtype,
                  int head_dim, void* stream);
 int launch_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t stride_elems,
                     const int32_t* slots, int64_t T, void* kc, void* vc, int32_t cache_dtype, int64_t num_slots,

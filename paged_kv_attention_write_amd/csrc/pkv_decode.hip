@@ -105,27 +105,42 @@ __device__ __forceinline__ void merge_store(void* __restrict__ out, int64_t oi, 
 }
 
 // One launch over all merge records (a 1-D grid of kMergeWaves-wave
-// workgroups).  The plan lists its wide records first (one row, at least
-// kWideMergeParts pieces): blocks [0, num_wide * hq) give each (wide record,
-// q head) a workgroup whose wave w folds parts w, w + kMergeWaves, ..., the
-// waves' states then combining through LDS (each scaled by 2^(m_w - M), an
-// empty wave contributing nothing).  The remaining blocks give each (record,
-// row, group of kMergeWaves q heads) a workgroup, one wave per head folding
-// all of its parts.
+// workgroups).  The plan lists its records in three kinds:
+//  - wide (one row, at least kWideMergeParts pieces): the first
+//    wide_slots * hq blocks give each (record, q head) a workgroup whose wave
+//    w folds parts w, w + kMergeWaves, ..., the waves' states then combining
+//    through LDS (each scaled by 2^(m_w - M), an empty wave adding nothing);
+//  - row blocks of chunk rows, then one-row records with few pieces: the
+//    next block_slots * max_rows * hgroups blocks and the last
+//    row_slots * hgroups blocks give each (record, row, group of kMergeWaves q
+//    heads) a workgroup, one wave per head folding all of its parts.
+// The live numbers of records come from `counts` in the workspace when it is
+// given (a launch sized for what any plan with these q_lens can hold, made
+// once and replayed for later plans), else from the arguments; blocks past
+// them exit.
 template <int QDT, int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __restrict__ merges,
                                                                  const float* __restrict__ po,
                                                                  const float* __restrict__ pl,
                                                                  void* __restrict__ out, int hq, float v_scale,
-                                                                 int num_wide, int max_rows) {
+                                                                 const int32_t* __restrict__ counts, int num_merges,
+                                                                 int num_wide, int num_block, int wide_slots,
+                                                                 int block_slots, int max_rows) {
     constexpr int E = D / 64;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t hd = static_cast<int64_t>(hq) * D;
     const const_ptr<float> lse = as_const(pl);
+    if (counts != nullptr) {
+        const const_ptr<int32_t> c = as_const(counts);
+        num_merges = c[0];
+        num_wide = c[1];
+        num_block = c[2];
+    }
     const int b = blockIdx.x;
-    const int wide_blocks = num_wide * hq;
+    const int wide_blocks = wide_slots * hq;
     if (b < wide_blocks) {
+        if (b / hq >= num_wide) return;
         __shared__ float sh_m[kMergeWaves], sh_s[kMergeWaves];
         __shared__ int sh_nan[kMergeWaves];
         __shared__ float sh_acc[kMergeWaves][D];
@@ -165,8 +180,17 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
     }
     const int hgroups = (hq + kMergeWaves - 1) / kMergeWaves;
     const int b2 = b - wide_blocks;
-    const int rec = num_wide + b2 / (max_rows * hgroups);
-    const int r = (b2 / hgroups) % max_rows;
+    const int block_blocks = block_slots * max_rows * hgroups;
+    int rec, r;
+    if (b2 < block_blocks) {
+        rec = num_wide + b2 / (max_rows * hgroups);
+        if (rec >= num_wide + num_block) return;
+        r = (b2 / hgroups) % max_rows;
+    } else {
+        rec = num_wide + num_block + (b2 - block_blocks) / hgroups;
+        if (rec >= num_merges) return;
+        r = 0;
+    }
     const int h = (b2 % hgroups) * kMergeWaves + wave;
     const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + rec);
     const int row0 = mw[0], nrows = mw[1], prow0 = mw[2], parts = mw[3];
@@ -244,28 +268,46 @@ int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, in
     return PKV_ERR_UNSUPPORTED;
 }
 
-int launch_merge(const AttnArgs& a, const Merge* merges, int num_merges, int num_wide, int max_rows, int q_dtype,
+int launch_merge(const AttnArgs& a, const pkv_plan* plan, const void* workspace, int max_rows, int q_dtype,
                  int head_dim, void* stream) {
-    if (num_merges == 0) return PKV_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const Merge* merges = reinterpret_cast<const Merge*>(static_cast<const char*>(workspace) + plan->off_merges);
+    // A launch made while the stream is being captured is replayed for later
+    // plans of the same room: it covers every record the room can hold and
+    // reads the live counts from the workspace.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool capturing = hipStreamIsCapturing(st, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+    const int32_t* counts = nullptr;
+    int64_t wide_slots = plan->num_wide_merges;
+    int64_t block_slots = plan->num_block_merges;
+    int64_t row_slots = static_cast<int64_t>(plan->num_merges) - wide_slots - block_slots;
+    if (capturing) {
+        counts = reinterpret_cast<const int32_t*>(static_cast<const char*>(workspace) + plan->off_queues) +
+                 plan_counts_index(plan->num_queues);
+        wide_slots = plan->max_row_merges;
+        block_slots = plan->max_block_merges;
+        row_slots = plan->max_row_merges;
+    }
     const int64_t hgroups = (a.hq + kMergeWaves - 1) / kMergeWaves;
-    const int64_t blocks = static_cast<int64_t>(num_wide) * a.hq +
-                           static_cast<int64_t>(num_merges - num_wide) * max_rows * hgroups;
+    const int64_t blocks = wide_slots * a.hq + block_slots * max_rows * hgroups + row_slots * hgroups;
+    if (blocks == 0) return PKV_OK;
     if (blocks > 0x7FFFFFFF) return PKV_ERR_SHAPE;
     const dim3 grid(static_cast<uint32_t>(blocks));
     const dim3 block(kMergeWaves * 64);
+    const int nm = plan->num_merges, nw = plan->num_wide_merges, nb = plan->num_block_merges;
+    const int ws = static_cast<int>(wide_slots), bsl = static_cast<int>(block_slots);
     if (q_dtype == PKV_DTYPE_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_F32, 64>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale, num_wide, max_rows);
+                           a.out, a.hq, a.v_scale, counts, nm, nw, nb, ws, bsl, max_rows);
     else if (q_dtype == PKV_DTYPE_F32)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_F32, 128>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale, num_wide, max_rows);
+                           a.out, a.hq, a.v_scale, counts, nm, nw, nb, ws, bsl, max_rows);
     else if (head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_BF16, 64>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale, num_wide, max_rows);
+                           a.out, a.hq, a.v_scale, counts, nm, nw, nb, ws, bsl, max_rows);
     else
         hipLaunchKernelGGL((merge_kernel<PKV_DTYPE_BF16, 128>), grid, block, 0, st, merges, a.partial_o, a.partial_lse,
-                           a.out, a.hq, a.v_scale, num_wide, max_rows);
+                           a.out, a.hq, a.v_scale, counts, nm, nw, nb, ws, bsl, max_rows);
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -68,10 +68,31 @@ static_assert(sizeof(Merge) == 16, "merge record is 16 bytes");
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
-// Planner (pkv_plan.cpp).  Pure host code.
+// Element counts of the sections of a plan image: units, int32 entries of
+// the queue-offset section (num_queues + prefill queues + 1 offsets, then
+// kPlanCounts live counts at a fixed index), merge records and partial rows.
+struct PlanSections {
+    int64_t units, queue_ints, merges, prows;
+};
+
+// The live counts that follow the queue offsets (index plan_counts_index):
+// merge records, wide records, row-block records.
+constexpr int kPlanCounts = 3;
+inline int64_t plan_counts_index(int32_t num_queues) {
+    return static_cast<int64_t>(1 + kPrefillQueuesPerQueue) * num_queues + 1;
+}
+
+// Section sizes that hold any plan over at most max_seqs sequences and
+// max_tokens query rows.
+PlanSections plan_capacity(int64_t max_seqs, int64_t max_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t num_queues);
+
+// Planner (pkv_plan.cpp).  Pure host code.  cap_seqs >= 0 lays the image
+// out at the offsets of plan_capacity(cap_seqs, cap_tokens, ...) instead of
+// the plan's own sizes.
 int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
-              size_t host_bytes, pkv_plan* plan);
+              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs = -1, int32_t cap_tokens = -1);
 
 // Upper bounds used by paged_attn_workspace_size.
 void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,

@@ -55,14 +55,36 @@ struct PrefillPiece {
 
 }  // namespace
 
+PlanSections plan_capacity(int64_t max_seqs, int64_t max_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t num_queues) {
+    const int64_t seqs = std::max<int64_t>(max_seqs, 0);
+    const int64_t toks = std::max<int64_t>(max_tokens, 0);
+    const int64_t nq = std::max<int32_t>(num_queues, 1);
+    // decode pieces: at most queues + requests (lazy fill).  Prefill row
+    // blocks: blocks of kPrefillQRows / G >= kPrefillQRows / num_q_heads
+    // rows, at most one partial block per sequence; a unit per kv head and
+    // piece.  A merge record per decode row or row block.
+    const int64_t hq = std::max<int32_t>(num_q_heads, 1);
+    const int64_t hkv = std::min<int64_t>(hq, std::max<int32_t>(num_kv_heads, 1));
+    const int64_t rmin = std::max<int64_t>(1, kPrefillQRows / hq);
+    const int64_t blocks = toks / rmin + seqs;
+    PlanSections c;
+    c.units = nq + seqs + blocks * kPrefillMaxPieces * hkv;
+    c.queue_ints = plan_counts_index(static_cast<int32_t>(nq)) + kPlanCounts;
+    c.merges = seqs + blocks;
+    c.prows = nq + seqs + toks * kPrefillMaxPieces;
+    return c;
+}
+
 int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
-              size_t host_bytes, pkv_plan* plan) {
+              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs, int32_t cap_tokens) {
     if (plan == nullptr || (num_seqs > 0 && ctx == nullptr)) return PKV_ERR_NULL;
     std::memset(plan, 0, sizeof(*plan));
     if (num_seqs < 0 || num_queues < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
         num_q_heads % num_kv_heads != 0)
         return PKV_ERR_SHAPE;
+    if (cap_seqs >= 0 && (num_seqs > cap_seqs || cap_tokens < 0)) return PKV_ERR_SHAPE;
 
     // Validate lengths and collect packed row offsets.
     std::vector<int32_t> row0(static_cast<size_t>(num_seqs) + 1, 0);
@@ -204,11 +226,24 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         }
     }
 
-    // wide merge records (one row, many pieces) first, each group in its order
-    std::stable_partition(merges.begin(), merges.end(),
-                          [](const Merge& m) { return m.nrows == 1 && m.parts >= kWideMergeParts; });
-    int32_t num_wide = 0;
-    for (const auto& m : merges) num_wide += (m.nrows == 1 && m.parts >= kWideMergeParts) ? 1 : 0;
+    // merge records: wide ones (one row, many pieces), then row blocks, then
+    // the other one-row records, each kind in its order
+    auto kind = [](const Merge& m) { return m.nrows > 1 ? 1 : (m.parts >= kWideMergeParts ? 0 : 2); };
+    std::stable_sort(merges.begin(), merges.end(),
+                     [&](const Merge& x, const Merge& y) { return kind(x) < kind(y); });
+    int32_t num_wide = 0, num_block = 0;
+    for (const auto& m : merges) {
+        num_wide += kind(m) == 0 ? 1 : 0;
+        num_block += kind(m) == 1 ? 1 : 0;
+    }
+    // records any plan with these q_lens can have: one per decode row, one
+    // per block of chunk rows
+    int64_t row_slots = 0, block_slots = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (L == 1) ++row_slots;
+        if (L > 1) block_slots += ceil_div(L, block_rows);
+    }
 
     int64_t num_units = 0;
     for (const auto& q : queues) num_units += static_cast<int64_t>(q.size());
@@ -219,14 +254,23 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     // Image: [units][queue offsets][merges], then the partial results.  The
     // decode queues' units come first, then the prefill queues'; the queue
     // offsets run over both (num_queues + prefill_queues + 1 entries).
-    const size_t units_bytes = align_up(static_cast<size_t>(num_units) * sizeof(Unit));
-    const size_t queues_bytes =
-        align_up((static_cast<size_t>(num_queues) + static_cast<size_t>(prefill_queues) + 1) * sizeof(int32_t));
-    const size_t merges_bytes = align_up(merges.size() * sizeof(Merge));
+    // Section sizes: the plan's own, or those of the capacity (the same
+    // offsets for every plan of that capacity, queues and heads).
+    PlanSections sec{num_units, plan_counts_index(num_queues) + kPlanCounts, static_cast<int64_t>(merges.size()),
+                     partial_rows};
+    if (cap_seqs >= 0) {
+        if (rows > cap_tokens) return PKV_ERR_SHAPE;
+        const PlanSections cap = plan_capacity(cap_seqs, cap_tokens, num_q_heads, num_kv_heads, num_queues);
+        if (num_units > cap.units || sec.merges > cap.merges || partial_rows > cap.prows) return PKV_ERR_SHAPE;
+        sec = cap;
+    }
+    const size_t units_bytes = align_up(static_cast<size_t>(sec.units) * sizeof(Unit));
+    const size_t queues_bytes = align_up(static_cast<size_t>(sec.queue_ints) * sizeof(int32_t));
+    const size_t merges_bytes = align_up(static_cast<size_t>(sec.merges) * sizeof(Merge));
     const size_t image = units_bytes + queues_bytes + merges_bytes;
-    const size_t po_bytes = align_up(static_cast<size_t>(partial_rows) * static_cast<size_t>(hd) * sizeof(float));
+    const size_t po_bytes = align_up(static_cast<size_t>(sec.prows) * static_cast<size_t>(hd) * sizeof(float));
     const size_t pl_bytes =
-        align_up(static_cast<size_t>(partial_rows) * static_cast<size_t>(num_q_heads) * sizeof(float));
+        align_up(static_cast<size_t>(sec.prows) * static_cast<size_t>(num_q_heads) * sizeof(float));
 
     plan->num_seqs = num_seqs;
     plan->num_tokens = static_cast<int32_t>(rows);
@@ -242,7 +286,9 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     plan->num_prefill_queues = prefill_queues;
     plan->num_prefill_units = static_cast<int32_t>(num_prefill_units);
     plan->num_wide_merges = num_wide;
-    plan->reserved0 = 0;
+    plan->num_block_merges = num_block;
+    plan->max_row_merges = static_cast<int32_t>(row_slots);
+    plan->max_block_merges = static_cast<int32_t>(std::min<int64_t>(block_slots, INT32_MAX));
     plan->off_units = 0;
     plan->off_queues = static_cast<int64_t>(units_bytes);
     plan->off_merges = static_cast<int64_t>(units_bytes + queues_bytes);
@@ -270,6 +316,10 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         for (const Unit& x : pqueues[q]) u[cursor++] = x;
     }
     qoff[num_queues + prefill_queues] = cursor;
+    int32_t* counts = qoff + plan_counts_index(num_queues);
+    counts[0] = static_cast<int32_t>(merges.size());
+    counts[1] = num_wide;
+    counts[2] = num_block;
     if (!merges.empty())
         std::memcpy(base + units_bytes + queues_bytes, merges.data(), merges.size() * sizeof(Merge));
     plan->magic = PKV_PLAN_MAGIC;
@@ -278,25 +328,14 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
 
 void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
                  int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes) {
-    const int64_t seqs = std::max<int32_t>(max_seqs, 0);
-    const int64_t toks = std::max<int32_t>(max_tokens, 0);
-    const int64_t nq = std::max<int32_t>(num_queues, 1);
-    // prefill row blocks: blocks of kPrefillQRows / G >= kPrefillQRows /
-    // num_q_heads rows, at most one partial block per sequence; a unit per kv
-    // head (<= num_q_heads) and piece
-    const int64_t hq = std::max<int32_t>(num_q_heads, 1);
-    const int64_t rmin = std::max<int64_t>(1, kPrefillQRows / hq);
-    const int64_t blocks = toks / rmin + seqs;
-    const int64_t prefill_units = blocks * kPrefillMaxPieces * hq;
-    const int64_t units = nq + seqs + prefill_units;
-    const int64_t merges = seqs + blocks;
-    const int64_t prows = nq + seqs + toks * kPrefillMaxPieces;
-    const size_t image = align_up(static_cast<size_t>(units) * sizeof(Unit)) +
-                         align_up(static_cast<size_t>((1 + kPrefillQueuesPerQueue) * nq + 1) * sizeof(int32_t)) +
-                         align_up(static_cast<size_t>(merges) * sizeof(Merge));
+    // a unit per kv head and piece: num_q_heads bounds the kv heads
+    const PlanSections c = plan_capacity(max_seqs, max_tokens, num_q_heads, num_q_heads, num_queues);
+    const size_t image = align_up(static_cast<size_t>(c.units) * sizeof(Unit)) +
+                         align_up(static_cast<size_t>(c.queue_ints) * sizeof(int32_t)) +
+                         align_up(static_cast<size_t>(c.merges) * sizeof(Merge));
     const size_t hd = static_cast<size_t>(std::max(num_q_heads, 1)) * static_cast<size_t>(std::max(head_dim, 1));
-    const size_t po = align_up(static_cast<size_t>(prows) * hd * sizeof(float));
-    const size_t pl = align_up(static_cast<size_t>(prows) * static_cast<size_t>(std::max(num_q_heads, 1)) * sizeof(float));
+    const size_t po = align_up(static_cast<size_t>(c.prows) * hd * sizeof(float));
+    const size_t pl = align_up(static_cast<size_t>(c.prows) * static_cast<size_t>(std::max(num_q_heads, 1)) * sizeof(float));
     if (workspace_bytes) *workspace_bytes = image + po + pl;
     if (host_bytes) *host_bytes = image;
 }

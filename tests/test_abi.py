@@ -92,11 +92,21 @@ def test_plan_partials_and_merges_are_consistent():
     _check_wide_first(p, merges)
 
 
-def _check_wide_first(p, merges):
-    """Wide merge records (one row, at least 4 pieces) are listed first and counted."""
-    wide = (merges[:, 1] == 1) & (merges[:, 3] >= 4)
-    nw = int(p.num_wide_merges)
-    assert nw == int(wide.sum()) and bool(np.all(wide[:nw])) and not bool(np.any(wide[nw:]))
+def _check_wide_first(p, merges, q_lens=None, group=4):
+    """Merge records come as wide ones (one row, at least 4 pieces), then row
+    blocks, then one-row records with few pieces, counted in the plan; the
+    room bounds follow from q_lens alone."""
+    kind = np.where(merges[:, 1] > 1, 1, np.where(merges[:, 3] >= 4, 0, 2))
+    assert np.all(np.diff(kind) >= 0)
+    assert int(p.num_wide_merges) == int((kind == 0).sum())
+    assert int(p.num_block_merges) == int((kind == 1).sum())
+    if q_lens is not None:
+        ql = np.asarray(q_lens)
+        assert int(p.max_row_merges) == int((ql == 1).sum())
+        rows = max(1, 128 // group)
+        assert int(p.max_block_merges) == int(sum(-(-int(L) // rows) for L in ql if L > 1))
+    assert int(p.num_wide_merges) <= int(p.max_row_merges)
+    assert int(p.num_block_merges) <= int(p.max_block_merges)
 
 
 @pytest.mark.parametrize("mix", ["uniform", "one-long", "heavy"])
@@ -107,7 +117,7 @@ def test_wide_merges_first_on_skew_mixes(mix, batch):
     lens = workloads.skew_lengths(mix, batch)
     p, image = pkv.plan_host(lens, None, 32, 8, 128, 256)
     _, _, merges = pkv.decode_plan_image(p, image)
-    _check_wide_first(p, merges)
+    _check_wide_first(p, merges, np.ones(batch, int))
 
 
 def _mixed_case():
@@ -142,7 +152,7 @@ def test_mixed_plan_covers_every_visible_pair_once():
                     cover[max(kind - 1, 0), r + i, lo:hi] += 1
         visible = np.arange(n)[None, :] <= (n - L + np.arange(L))[:, None]
         assert np.array_equal(cover, np.broadcast_to(visible.astype(np.int32), cover.shape)), s
-    _check_wide_first(p, merges)
+    _check_wide_first(p, merges, ql)
     # every merged block lists its pieces at prow0 + c * nrows
     for row0, nrows, prow0, parts in merges:
         us = units[(units[:, 3] == row0) & (units[:, 6] >= 0)]
