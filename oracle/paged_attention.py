@@ -7,7 +7,10 @@ architecture diagram; "How to design an LLM serving system", "PagedAttention"):
 
 * ``k_cache``, ``v_cache``: ``[num_blocks, block_size, H_kv, D]`` storage arrays.
 * ``block_tables``: int32 ``[B, max_blocks]``; row ``s`` lists the physical
-  block of each logical block of sequence ``s``.
+  block of each logical block of sequence ``s``.  Or, in the CSR form of
+  "How Easy Is It to Start Serving LLMs?" (Phase 4 §1: ``kv_indptr`` and
+  ``kv_indices``), a flat int32 ``kv_indices`` array whose slice
+  ``kv_indptr[s]:kv_indptr[s+1]`` is the row of sequence ``s``.
 * ``slot_mapping``: int32 ``[T]``; token ``t`` of this step goes to physical
   slot ``slot_mapping[t]`` = ``block * block_size + offset``.
 * ``q``: ``[T, Hq, D]`` packed tokens; sequence ``s`` owns rows
@@ -154,8 +157,13 @@ def paged_attention(
     k_scale: float = 1.0,
     v_scale: float = 1.0,
     seqs=None,
+    kv_indptr=None,
 ):
     """Exact attention over a paged cache; returns ``(out, lse)`` in fp64.
+
+    With ``kv_indptr`` given, ``block_tables`` is the flat ``kv_indices``
+    array and sequence ``s`` reads its pages from
+    ``kv_indices[kv_indptr[s]:kv_indptr[s+1]]`` (the CSR page table).
 
     For every sequence ``s`` (or only those listed in ``seqs``): gather its
     ``n = context_lens[s]`` keys and values through the block table, decode
@@ -194,8 +202,12 @@ def paged_attention(
             continue
         if L > n:
             raise ValueError(f"sequence {s}: {L} query rows but only {n} keys")
-        ks = decode_storage(gather_kv(k_cache, block_tables[s], n), kv_dtype, k_scale)
-        vs = decode_storage(gather_kv(v_cache, block_tables[s], n), kv_dtype, v_scale)
+        if kv_indptr is None:
+            row = block_tables[s]
+        else:
+            row = np.asarray(block_tables)[int(kv_indptr[s]):int(kv_indptr[s + 1])]
+        ks = decode_storage(gather_kv(k_cache, row, n), kv_dtype, k_scale)
+        vs = decode_storage(gather_kv(v_cache, row, n), kv_dtype, v_scale)
         pos = n - L + np.arange(L)
         for h in range(hq):
             g = h // group

@@ -330,3 +330,33 @@ def test_fp8_attention_reads_dequantised_values():
                       nx.e4m3_decode(Vq[0], float(vs)).tolist(), n, float(np.float32(0.3)), 4, h)
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
     assert Kd[0].shape == Kb[0].shape
+
+
+def _to_csr(tables, lens, bs, extra=0, seed=0):
+    """CSR page table of dense rows: each sequence's first ceil(n/bs) entries,
+    plus ``extra`` unused entries (-1) after them."""
+    rows = []
+    for s, n in enumerate(lens):
+        nb = -(-int(n) // bs)
+        rows.append(np.concatenate([tables[s, :nb], np.full(extra, -1, np.int32)]).astype(np.int32))
+    indptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    return indptr, np.concatenate(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("bs,extra", [(1, 0), (4, 2), (16, 0), (16, 3)])
+def test_csr_page_table_equals_dense(bs, extra):
+    """The CSR form of the page table ("How Easy Is It to Start Serving LLMs?",
+    Phase 4 §1) reads the same pages as the dense rows: bit-identical outputs,
+    also with unused entries after a row's last page and an empty sequence."""
+    lens = [5, 37, 100, 0, 64]
+    q_lens = [1, 1, 3, 0, 1]
+    K, V, _ = _single(lens, 4, 2, 16, bs, seed=9, kv_dtype="bf16")
+    kp, vp, t = page_out(K, V, bs, perm_seed=bs * 7, extra_blocks=4)
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal((sum(q_lens), 4, 16)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    ref, ref_lse = oracle.paged_attention(q, "f32", kp, vp, "bf16", t, np.asarray(lens, np.int32), cu, 0.25)
+    indptr, indices = _to_csr(t, lens, bs, extra)
+    got, got_lse = oracle.paged_attention(q, "f32", kp, vp, "bf16", indices, np.asarray(lens, np.int32), cu, 0.25,
+                                          kv_indptr=indptr)
+    assert np.array_equal(got, ref) and np.array_equal(got_lse, ref_lse)
