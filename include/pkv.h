@@ -298,6 +298,37 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
                      float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/*
+ * paged_attn_decode_csr / paged_attn_mixed_csr - paged_attn_decode and
+ * paged_attn_mixed with the page table in CSR form ("How Easy Is It to Start
+ * Serving LLMs?", Phase 4 §1: kv_indptr / kv_indices): sequence s reads the
+ * page of its logical block b from kv_indices[kv_indptr[s] + b], for
+ * b < kv_indptr[s+1] - kv_indptr[s]; a row may hold unused entries after its
+ * last page, and rows of different sequences may name the same pages.
+ *   kv_indptr   int32 [num_seqs + 1], device, non-decreasing, kv_indptr[0] >= 0
+ *   kv_indices  int32 [kv_indptr[num_seqs]], device (non-NULL)
+ * Every other argument, the plan and the workspace as for the dense forms.
+ * The offsets are read on the device and not checked there: kv_indptr must
+ * stay within kv_indices (a caller error otherwise, like a short dense row).
+ * A key whose logical block is past its row, or whose entry is outside the
+ * pool, makes its sequence's rows NaN, as with dense tables.
+ * Errors as paged_attn_decode / paged_attn_mixed (PKV_ERR_NULL for a NULL
+ * kv_indptr or kv_indices with rows to compute).
+ */
+int paged_attn_decode_csr(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                          const void* v_cache, int32_t kv_dtype, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                          int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+int paged_attn_mixed_csr(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                         const void* v_cache, int32_t kv_dtype, const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                         const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

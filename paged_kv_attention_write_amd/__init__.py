@@ -23,6 +23,8 @@ from ._abi import (  # noqa: F401
     lib,
     paged_attn_decode,
     paged_attn_mixed,
+    paged_attn_decode_csr,
+    paged_attn_mixed_csr,
     paged_kv_write,
     plan_host,
     strerror,

@@ -46,6 +46,8 @@ EXPORTS = (
     "paged_attn_plan_capacity",
     "paged_attn_decode",
     "paged_attn_mixed",
+    "paged_attn_decode_csr",
+    "paged_attn_mixed_csr",
 )
 
 
@@ -121,6 +123,13 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_mixed.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
                                        i32, f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_mixed.restype = ctypes.c_int
+        # CSR forms: kv_indptr, kv_indices in place of block_tables, max_blocks
+        L.paged_attn_decode_csr.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i64, i32,
+                                            f32, f32, f32, P(PkvPlan), vp, sz, vp]
+        L.paged_attn_decode_csr.restype = ctypes.c_int
+        L.paged_attn_mixed_csr.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           i64, i32, f32, f32, f32, P(PkvPlan), vp, sz, vp]
+        L.paged_attn_mixed_csr.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -360,6 +369,57 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                      float(v_scale), ctypes.byref(plan.desc), _ptr(plan.workspace),
                                      plan.workspace.numel(), _stream(stream, q.device))
     _check(st, "paged_attn_decode")
+
+
+def _csr_check(kv_indptr, kv_indices, B):
+    torch = _torch()
+    if kv_indptr.dtype != torch.int32 or kv_indptr.dim() != 1 or kv_indptr.shape[0] != B + 1 or \
+            not kv_indptr.is_contiguous():
+        raise ValueError("kv_indptr must be contiguous int32 [B+1]")
+    if kv_indices.dtype != torch.int32 or kv_indices.dim() != 1 or not kv_indices.is_contiguous():
+        raise ValueError("kv_indices must be contiguous int32 [nnz]")
+
+
+def paged_attn_decode_csr(out, q, k_cache, v_cache, kv_indptr, kv_indices, context_lens, scale: float, plan: Plan,
+                          k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """``paged_attn_decode`` with the page table in CSR form: sequence ``s``
+    reads its pages from ``kv_indices[kv_indptr[s]:kv_indptr[s+1]]``."""
+    torch = _torch()
+    B, hq = q.shape[0], q.shape[1]
+    dummy = kv_indices.view(1, -1) if kv_indices.numel() else kv_indices.new_zeros((1, 1))
+    nb, bs, hkv, d = _attn_common(q, k_cache, v_cache, dummy, context_lens, plan)
+    _csr_check(kv_indptr, kv_indices, B)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    with torch.cuda.device(q.device):
+        st = lib().paged_attn_decode_csr(_ptr(out), _ptr(q), dtype_code(q), q.stride(0) if B else hq * d,
+                                         _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(kv_indptr),
+                                         _ptr(dummy), _ptr(context_lens), B, hq, hkv, d, nb, bs, float(scale),
+                                         float(k_scale), float(v_scale), ctypes.byref(plan.desc),
+                                         _ptr(plan.workspace), plan.workspace.numel(), _stream(stream, q.device))
+    _check(st, "paged_attn_decode_csr")
+
+
+def paged_attn_mixed_csr(out, q, k_cache, v_cache, kv_indptr, kv_indices, cu_seqlens, context_lens, scale: float,
+                         plan: Plan, k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> None:
+    """``paged_attn_mixed`` with the page table in CSR form."""
+    torch = _torch()
+    T, hq = q.shape[0], q.shape[1]
+    B = context_lens.shape[0]
+    dummy = kv_indices.view(1, -1) if kv_indices.numel() else kv_indices.new_zeros((1, 1))
+    nb, bs, hkv, d = _attn_common(q, k_cache, v_cache, dummy, context_lens, plan)
+    _csr_check(kv_indptr, kv_indices, B)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.shape[0] != B + 1:
+        raise ValueError("cu_seqlens must be int32 [B+1]")
+    with torch.cuda.device(q.device):
+        st = lib().paged_attn_mixed_csr(_ptr(out), _ptr(q), dtype_code(q), q.stride(0) if T else hq * d,
+                                        _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(kv_indptr),
+                                        _ptr(dummy), _ptr(cu_seqlens), _ptr(context_lens), B, T, hq, hkv, d, nb, bs,
+                                        float(scale), float(k_scale), float(v_scale), ctypes.byref(plan.desc),
+                                        _ptr(plan.workspace), plan.workspace.numel(), _stream(stream, q.device))
+    _check(st, "paged_attn_mixed_csr")
 
 
 def paged_attn_mixed(out, q, k_cache, v_cache, block_tables, cu_seqlens, context_lens, scale: float, plan: Plan,

@@ -90,6 +90,7 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     a.v_cache = v_cache;
     a.block_tables = block_tables;
     a.max_blocks = max_blocks;
+    a.kv_indptr = nullptr;
     a.context_lens = context_lens;
     a.hq = hq;
     a.hkv = hkv;
@@ -233,12 +234,16 @@ int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_
     return PKV_OK;
 }
 
-int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
-                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
-                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
-                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
-                      int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Decode over dense rows (kv_indptr null) or CSR rows (block_tables holds
+// kv_indices, max_blocks_per_seq is unused).
+static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                       const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* kv_indptr, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
                              max_blocks_per_seq, context_lens, num_seqs, num_seqs, num_q_heads, num_kv_heads,
                              head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan, workspace,
@@ -246,13 +251,42 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
     if (st != PKV_OK) return st;
     if (plan->max_q_len > 1) return PKV_ERR_PLAN;
     if (num_seqs == 0) return PKV_OK;
-    const AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
-                                 max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, num_blocks, block_size,
-                                 scale, k_scale, v_scale, plan, workspace);
+    AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                           context_lens, num_q_heads, num_kv_heads, num_blocks, block_size, scale, k_scale, v_scale,
+                           plan, workspace);
+    a.kv_indptr = kv_indptr;
     st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
     if (st != PKV_OK) return st;
     return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
 }
+
+extern "C" {
+
+int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                      int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (block_tables == nullptr && num_seqs > 0) return PKV_ERR_NULL;
+    return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                       nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_csr(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                          const void* v_cache, int32_t kv_dtype, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* context_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                          int32_t block_size, float scale, float k_scale, float v_scale, const pkv_plan* plan,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && (kv_indptr == nullptr || kv_indices == nullptr)) return PKV_ERR_NULL;
+    return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, kv_indices, 1, kv_indptr,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, scale,
+                       k_scale, v_scale, plan, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
 
 // Most rows of any merge record: decode merges have one, prefill merges a row block.
 static int merge_rows(const pkv_plan* plan, int group) {
@@ -260,13 +294,13 @@ static int merge_rows(const pkv_plan* plan, int group) {
     return std::max(1, std::min(plan->max_q_len, std::max(1, kPrefillQRows / group)));
 }
 
-int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
-                     const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
-                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens, const int32_t* context_lens,
-                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
-                     float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* kv_indptr, const int32_t* cu_seqlens,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale,
+                      float k_scale, float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                      void* stream) {
     int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
                              max_blocks_per_seq, context_lens, num_seqs, num_tokens, num_q_heads, num_kv_heads,
                              head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan, workspace,
@@ -274,9 +308,10 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
     if (st != PKV_OK) return st;
     if (num_tokens == 0) return PKV_OK;
     if (cu_seqlens == nullptr) return PKV_ERR_NULL;
-    const AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
-                                 max_blocks_per_seq, context_lens, num_q_heads, num_kv_heads, num_blocks, block_size,
-                                 scale, k_scale, v_scale, plan, workspace);
+    AttnArgs a = make_args(out, q, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                           context_lens, num_q_heads, num_kv_heads, num_blocks, block_size, scale, k_scale, v_scale,
+                           plan, workspace);
+    a.kv_indptr = kv_indptr;
     const int group = num_q_heads / num_kv_heads;
     const bool chunks = plan->num_prefill_units > 0;
     if (chunks && !prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
@@ -298,6 +333,33 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
         if (st != PKV_OK) return st;
     }
     return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
+}
+
+extern "C" {
+
+int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                     const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
+                     float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    if (block_tables == nullptr && num_tokens > 0) return PKV_ERR_NULL;
+    return mixed_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                      nullptr, cu_seqlens, context_lens, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                      num_blocks, block_size, scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_mixed_csr(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
+                         const void* v_cache, int32_t kv_dtype, const int32_t* kv_indptr, const int32_t* kv_indices,
+                         const int32_t* cu_seqlens, const int32_t* context_lens, int32_t num_seqs,
+                         int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                         const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_tokens > 0 && (kv_indptr == nullptr || kv_indices == nullptr)) return PKV_ERR_NULL;
+    return mixed_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, kv_indices, 1, kv_indptr,
+                      cu_seqlens, context_lens, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                      block_size, scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

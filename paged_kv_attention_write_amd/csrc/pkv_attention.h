@@ -14,8 +14,9 @@ struct AttnArgs {
     int64_t q_stride;             // elements
     const void* k_cache;          // [num_blocks][block_size][hkv][D]
     const void* v_cache;
-    const int32_t* block_tables;  // [B][max_blocks]
+    const int32_t* block_tables;  // [B][max_blocks], or the CSR entries kv_indices
     int32_t max_blocks;
+    const int32_t* kv_indptr;     // [B + 1] CSR row offsets into block_tables, or null (dense rows)
     const int32_t* context_lens;  // [B]
     int32_t hq;
     int32_t hkv;
@@ -36,6 +37,30 @@ __device__ __forceinline__ int page_of(const AttnArgs& a, int t) {
     return a.block_shift >= 0 ? t >> a.block_shift : t / a.block_size;
 }
 __device__ __forceinline__ int row_in_page(const AttnArgs& a, int t, int pidx) { return t - pidx * a.block_size; }
+
+// The page-table row of one sequence: its entries and their number.  Dense
+// tables give every sequence max_blocks entries; a CSR table ("How Easy Is It
+// to Start Serving LLMs?", Phase 4 §1: kv_indptr / kv_indices) gives sequence
+// s the entries kv_indptr[s] .. kv_indptr[s+1] - 1.  An empty CSR row points
+// at kv_indptr[0] (so that a clamped read stays in bounds) with n = 0, which
+// makes every page of it invalid.
+struct SeqTable {
+    const_ptr<int32_t> p;
+    int32_t n;
+    // entry i clamped into the row (read unconditionally; the caller checks i < n)
+    __device__ __forceinline__ int32_t clamped(int i) const { return p[max(0, min(i, n - 1))]; }
+    __device__ __forceinline__ int32_t operator[](int i) const { return p[i]; }
+};
+
+__device__ __forceinline__ SeqTable seq_table(const AttnArgs& a, int seq) {
+    if (a.kv_indptr != nullptr) {
+        const const_ptr<int32_t> ip = as_const(a.kv_indptr);
+        const int32_t b = ip[seq];
+        const int32_t n = ip[seq + 1] - b;
+        return n > 0 ? SeqTable{as_const(a.block_tables) + b, n} : SeqTable{ip, 0};
+    }
+    return SeqTable{as_const(a.block_tables) + static_cast<int64_t>(seq) * a.max_blocks, a.max_blocks};
+}
 
 __device__ __forceinline__ Unit load_unit(const_ptr<Unit> units, int i) {
     const const_ptr<int32_t> w = reinterpret_cast<const_ptr<int32_t>>(units + i);

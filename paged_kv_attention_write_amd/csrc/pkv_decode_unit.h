@@ -111,12 +111,12 @@ constexpr int kSubTiles = U >= 4 ? U / 4 : 1;
 // table): scalar loads, issued a tile ahead of their use.
 template <int U>
 __device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const AttnArgs& a,
-                                           const_ptr<int32_t> tbl, int t0, int ke) {
+                                           const SeqTable& tbl, int t0, int ke) {
 #pragma unroll
     for (int s = 0; s < kSubTiles<U>; ++s) {
         const int ts = t0 + 16 * s;
         const int pidx = page_of(a, ts);
-        pages[s] = (ts < ke && pidx < a.max_blocks) ? tbl[pidx] : -1;
+        pages[s] = (ts < ke && pidx < tbl.n) ? tbl[pidx] : -1;
     }
 }
 
@@ -125,14 +125,14 @@ __device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const
 // read unconditionally at a clamped index.  (Reading them a tile ahead was
 // measured slower on one-token pages.)
 template <int U>
-__device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, const_ptr<int32_t> tbl, int t0,
+__device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, const SeqTable& tbl, int t0,
                                            int lim, int ke, int row) {
     const int last = page_of(a, ke - 1);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int t = t0 + 4 * u + row;
         const int pidx = t < lim ? page_of(a, t) : last;
-        lp[u] = tbl[min(pidx, a.max_blocks - 1)];
+        lp[u] = tbl.clamped(pidx);
     }
 }
 
@@ -140,7 +140,8 @@ template <int KVDT, int D, int U, int KW, bool UNIFORM_PAGE, bool FULL>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
                                           const int32_t (&pages)[kSubTiles<U>], const int32_t (&lp)[U],
                                           const char* kc, const char* vc, int t0, int ke, int row, uint32_t lane_off,
-                                          uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, bool& bad) {
+                                          uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, int tbl_n,
+                                          bool& bad) {
     const int bs = a.block_size;
     // block ids are int32: a pool of more than 2^31 - 1 blocks is addressed up to that many
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
@@ -185,7 +186,7 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
             const bool tv = FULL || t < ke;
             const int pidx = page_of(a, t);
             const uint32_t page = static_cast<uint32_t>(lp[u]);
-            const bool ok = tv && pidx < a.max_blocks && page < nblocks;  // a negative id wraps to >= 2^31
+            const bool ok = tv && pidx < tbl_n && page < nblocks;  // a negative id wraps to >= 2^31
             bad |= tv && !ok;
             const uint64_t slot = static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
                                   static_cast<uint32_t>(row_in_page(a, t, pidx));
@@ -199,13 +200,13 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
 // Byte offset (inside a pool) of the clamp token of a piece ending at ke:
 // key ke - 1 of the sequence, at the lane's head offset, or the head offset
 // alone when that key's page is outside the pool.
-__device__ __forceinline__ int64_t clamp_offset(const AttnArgs& a, const_ptr<int32_t> tbl, int ke,
+__device__ __forceinline__ int64_t clamp_offset(const AttnArgs& a, const SeqTable& tbl, int ke,
                                                 uint32_t head_off, int64_t tok_bytes) {
     const int bs = a.block_size;
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     const int t = ke - 1;
     const int pidx = page_of(a, t);
-    const uint32_t page = static_cast<uint32_t>(pidx < a.max_blocks ? tbl[pidx] : -1);
+    const uint32_t page = static_cast<uint32_t>(pidx < tbl.n ? tbl[pidx] : -1);
     if (page >= nblocks) return head_off;
     return static_cast<int64_t>(static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
                                 static_cast<uint32_t>(row_in_page(a, t, pidx))) * tok_bytes + head_off;
@@ -312,7 +313,7 @@ struct DecodeRun {
     // the unit
     Unit un;
     int n, n_dev, kb, ke, h;
-    const_ptr<int32_t> tbl;
+    SeqTable tbl;
     uint32_t head_off, lane_off;
     int64_t clamp_off;
     // softmax state of this wave's head
@@ -350,7 +351,7 @@ struct DecodeRun {
         n_dev = as_const(a.context_lens)[u.seq];
         kb = u.kv_begin;
         ke = min(u.kv_end, n);
-        tbl = as_const(a.block_tables) + static_cast<int64_t>(u.seq) * a.max_blocks;
+        tbl = seq_table(a, u.seq);
         const char* qbase = static_cast<const char*>(a.q) +
                             (static_cast<int64_t>(u.row0) * a.q_stride + static_cast<int64_t>(h) * G * D +
                              col * EPL) * QB;
@@ -397,10 +398,10 @@ struct DecodeRun {
             if constexpr (!UNIFORM_PAGE) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
             if (t0 + TT <= tb) {
                 load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
-                                                              head_off, tok_bytes, clamp_off, bad);
+                                                              head_off, tok_bytes, clamp_off, tbl.n, bad);
             } else {
                 load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
-                                                               head_off, tok_bytes, clamp_off, bad);
+                                                               head_off, tok_bytes, clamp_off, tbl.n, bad);
             }
             if constexpr (UNIFORM_PAGE) {
                 if (t0 + step < tb) {

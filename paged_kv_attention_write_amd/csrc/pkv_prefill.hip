@@ -94,11 +94,11 @@ struct PfRole {
 };
 
 // Table entry of the page of key t, read unconditionally at an index clamped
-// into the sequence's row (max_blocks >= 1): every thread issues the same
+// into the sequence's row: every thread issues the same
 // loads in the same order, so the waits for them count in order and none is
 // taken right after its load.  pf_load decides whether the entry is valid.
-__device__ __forceinline__ int32_t pf_page(const AttnArgs& a, const_ptr<int32_t> tbl, int t) {
-    return tbl[min(page_of(a, t), a.max_blocks - 1)];
+__device__ __forceinline__ int32_t pf_page(const AttnArgs& a, const SeqTable& tbl, int t) {
+    return tbl.clamped(page_of(a, t));
 }
 
 template <int KVDT, int D>
@@ -113,14 +113,14 @@ struct PfRegs {
 // staged as zeros, and a page outside the pool flags the unit.
 template <int KVDT, int D>
 __device__ __forceinline__ void pf_load(PfRegs<KVDT, D>& r, const AttnArgs& a, const PfRole<D>& role, int h,
-                                        int t, int kend, int32_t page, bool& bad) {
+                                        int t, int kend, int32_t page, int tbl_n, bool& bad) {
     constexpr int KVB = dt_bytes(KVDT);
     constexpr int W = PfItem<KVDT>::W;
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     const int pidx = page_of(a, t);
     const bool tv = role.active && t < kend;
     // a key past the table, or a negative id (wraps to >= 2^31), is invalid
-    const bool ok = tv && pidx < a.max_blocks && static_cast<uint32_t>(page) < nblocks;
+    const bool ok = tv && pidx < tbl_n && static_cast<uint32_t>(page) < nblocks;
     bad |= tv && !ok;
     const int64_t slot = static_cast<int64_t>(page) * a.block_size + row_in_page(a, t, pidx);
     const int64_t off = ok ? ((slot * a.hkv + h) * D + role.dg * 8) * KVB : 0;
@@ -298,7 +298,7 @@ struct PfWave {
     int n, g4, r, hq_idx, pos, h, kb, kend;
     bool row_ok, wave_has_rows, wave_full;
     int wave_first_pos, wave_last_pos;
-    const_ptr<int32_t> tbl;
+    SeqTable tbl;
     bf16x8_t qb[NS];
     float qk;
     f32x4_t acc[ND];
@@ -327,7 +327,7 @@ struct PfWave {
         const int n_ctx = as_const(a.context_lens)[un.seq];
         kb = un.kv_begin;
         kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
-        tbl = as_const(a.block_tables) + static_cast<int64_t>(un.seq) * a.max_blocks;
+        tbl = seq_table(a, un.seq);
 
         // q slice of this lane's pair: elements 32 s + 8 g4 .. + 7
         const char* qrow = static_cast<const char*>(a.q) +
@@ -415,18 +415,18 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
         PfWave<D, G> W;
         W.open(a, un, wave, lane);
         const int kb = W.kb, kend = W.kend, h = W.h;
-        const const_ptr<int32_t> tbl = W.tbl;
+        const SeqTable tbl = W.tbl;
 
         // prologue: tile 0 staged; tiles 1 and 2 and the pages of tiles 3
         // and 4 in flight
         PfRegs<KVDT, D> ra, rb;
         __syncthreads();  // the LDS of the previous unit is free
-        pf_load<KVDT, D>(ra, a, role, h, kb + role.kk, kend, pf_page(a, tbl, kb + role.kk), W.bad);
+        pf_load<KVDT, D>(ra, a, role, h, kb + role.kk, kend, pf_page(a, tbl, kb + role.kk), tbl.n, W.bad);
         pf_stage<KVDT, D>(ra, role, lds, 0);
         pf_load<KVDT, D>(ra, a, role, h, kb + kPfKeys + role.kk, kend, pf_page(a, tbl, kb + kPfKeys + role.kk),
-                         W.bad);
+                         tbl.n, W.bad);
         pf_load<KVDT, D>(rb, a, role, h, kb + 2 * kPfKeys + role.kk, kend,
-                         pf_page(a, tbl, kb + 2 * kPfKeys + role.kk), W.bad);
+                         pf_page(a, tbl, kb + 2 * kPfKeys + role.kk), tbl.n, W.bad);
         int32_t pa = pf_page(a, tbl, kb + 3 * kPfKeys + role.kk);
         int32_t pb = pf_page(a, tbl, kb + 4 * kPfKeys + role.kk);
         __syncthreads();
@@ -443,7 +443,7 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
             // waits count in order
             pf_stage<KVDT, D>(rs, role, lds, buf ^ 1);
             const int t3 = t0 + 3 * kPfKeys + role.kk;
-            pf_load<KVDT, D>(rs, a, role, h, t3, kend, pg, W.bad);
+            pf_load<KVDT, D>(rs, a, role, h, t3, kend, pg, tbl.n, W.bad);
             pg = pf_page(a, tbl, t3 + 2 * kPfKeys);
             __syncthreads();
         };
@@ -519,7 +519,7 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
         PfWave<D, G> W;
         W.open(a, un, wave, lane);
         const int kb = W.kb, kend = W.kend, h = W.h;
-        const const_ptr<int32_t> tbl = W.tbl;
+        const SeqTable tbl = W.tbl;
         const int ntiles = kend > kb ? (kend - kb + kPfKeys - 1) / kPfKeys : 0;
         const int glast = kend > kb ? ((kend - 1) & ~15) : kb;  // start of the unit's last 16 keys
 
@@ -528,7 +528,7 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
         // page-table entry (index clamped into the row; validity is decided
         // at the load)
         auto half = [&](int t0, int f) { return min(t0 + 16 * f, glast); };
-        auto entry = [&](int t0, int f) { return tbl[min(half(t0, f) >> shift, a.max_blocks - 1)]; };
+        auto entry = [&](int t0, int f) { return tbl.clamped(half(t0, f) >> shift); };
         struct Entries {
             int32_t e0, e1;
         };
@@ -539,7 +539,7 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
                 const int g = half(t0, f);
                 const int32_t ef = f ? e.e1 : e.e0;
                 const int pidx = g >> shift;
-                const bool ok = pidx < a.max_blocks && static_cast<uint32_t>(ef) < nblocks;
+                const bool ok = pidx < tbl.n && static_cast<uint32_t>(ef) < nblocks;
                 W.bad |= t0 + 16 * f < kend && !ok;
                 const int64_t row0 = static_cast<int64_t>(ok ? ef : 0) * a.block_size + (g - (pidx << shift));
                 __builtin_amdgcn_global_load_lds(lane_src + (row0 * a.hkv + h) * (D * 2),
