@@ -13,9 +13,13 @@ scattered-vs-contiguous comparison), ``fp8prefix`` (128 sequences over a
 shared 4096-token prefix, fp8 cache), ``mixed`` (63 decodes and one 512-row
 prefill chunk packed in one step; "nanoserve" chunked prefill) and
 ``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
-peak).  ``--study skew`` and ``--study plan-cost`` print, instead of the bench
-line, one JSON line per case of the load-balance study (length mixes of equal
-total tokens at batch 4-128) and of the planner-cost sweep (batch 8-512).
+peak), ``specverify`` (64 sequences with 4 new rows each, a speculative
+verify step, through the mixed path).  ``--study skew``, ``--study
+plan-cost`` and ``--study pages`` print, instead of the bench line, one JSON
+line per case of the load-balance study (length mixes of equal total tokens
+at batch 4-128), the planner-cost sweep (batch 8-512) and the page-size
+sweep (pages of 1/4/16/64 tokens and a contiguous slab at 64 x 4K,
+16 x 16K and 256 x 1K keys).
 
 Inputs are synthetic: block tables, lengths and slots come from the seeded
 generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
@@ -64,6 +68,9 @@ CONFIGS = {
     "mixed": dict(config="mixed", layout="page16",
                   desc="63 decodes (ctx U[256,2048]) + one 512-row chunk over 2048 cached tokens, packed T=575, "
                        "32q/8kv, D=128, page 16, bf16"),
+    "specverify": dict(config="decode", layout="page16", q_len=4,
+                       desc="64 seqs x 4 new rows each (speculative verify), ctx U[512,4096], 32q/8kv, D=128, "
+                            "page 16, bf16; all rows through the mixed path"),
     "mixed-chunk": dict(config="mixed", layout="page16", only_chunk=True,
                         desc="the 512-row chunk of the mixed step alone (2560 keys, causal), 32q/8kv, D=128, bf16"),
 }
@@ -285,6 +292,53 @@ def study_skew(args, torch, pkv, workloads, byte_model):
             torch.cuda.empty_cache()
 
 
+def study_pages(args, torch, pkv, workloads, byte_model):
+    """Page-size sweep: decode over equal-length batches of the pages' three
+    shapes (64 x 4096, 16 x 16384, 256 x 1024 keys), pages of 1, 4, 16 and 64
+    tokens in shuffled order and one contiguous slab (page 16 in order), one
+    JSON line per case."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    for batch, n in ((64, 4096), (16, 16384), (256, 1024)):
+        ref_us = None
+        for layout, bs in (("contiguous", 16), ("shuffled", 1), ("shuffled", 4), ("shuffled", 16), ("shuffled", 64)):
+            lens = np.full(batch, n, np.int32)
+            st = workloads.structure_for_lengths(workloads.CONFIG_IDS["skew"], lens, block_size=bs,
+                                                 layout="identity" if layout == "contiguous" else "shuffle")
+            layers = build_layers(torch, st, {"config": "decode"}, args.layers, dev)
+            tables = torch.from_numpy(st["block_tables"]).to(dev)
+            ctx = torch.from_numpy(st["context_lens"]).to(dev)
+            plan = pkv.Plan(lens, None, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                            num_queues=args.queues)
+            cnt = args.steps * len(layers)
+            ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(cnt)]
+            ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(cnt)]
+            for it in range(args.warmup + args.steps):
+                for l, layer in enumerate(layers):
+                    k = (it - args.warmup) * len(layers) + l
+                    if k >= 0:
+                        ev_a[k].record(stream)
+                    pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan)
+                    if k >= 0:
+                        ev_b[k].record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+            nbytes = byte_model.attention_bytes(lens, st["q_lens"], 32, 8, 128, bs, 2, 2)
+            p50 = float(np.median(ms)) * 1e-3
+            if layout == "contiguous":
+                ref_us = p50
+            print(json.dumps({
+                "study": "pages", "batch": batch, "context": n, "layout": layout, "block_size": bs,
+                "table_entries": int(st["block_tables"].size),
+                "call_us": {"p10": round(float(np.percentile(ms, 10)) * 1e3, 2), "p50": round(p50 * 1e6, 2),
+                            "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
+                "TBps": round(nbytes / p50 / 1e12, 4), "frac_of_8TBps": round(nbytes / p50 / 8e12, 4),
+                "vs_contiguous": round(ref_us / p50, 4), "layers": len(layers)}), flush=True)
+            del layers, plan, tables
+            torch.cuda.empty_cache()
+
+
 def study_plan_cost(args, torch, pkv, workloads):
     """Host planner cost per step (reused by all layers) for batch 8..512 with
     context uniform in [512, 4096], one JSON line per batch."""
@@ -321,7 +375,7 @@ def main():
                     help="time the step only as eager launches (by default the step is also captured once as a "
                          "HIP graph of every layer's write + attention, the plan made for a fixed capacity, and "
                          "replayed after each step's re-plan; value and ms_per_step then come from the replays)")
-    ap.add_argument("--study", choices=["skew", "plan-cost"],
+    ap.add_argument("--study", choices=["skew", "plan-cost", "pages"],
                     help="instead of the bench line: the load-balance study over length mixes (skew) or the "
                          "planner cost over batch sizes (plan-cost), one JSON line per case")
     args = ap.parse_args()
@@ -346,11 +400,18 @@ def main():
     if args.study == "plan-cost":
         study_plan_cost(args, torch, pkv, workloads)
         return
+    if args.study == "pages":
+        study_pages(args, torch, pkv, workloads, byte_model)
+        return
 
     cfg = CONFIGS[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     st = workloads.structure_only(cfg["config"], cfg["layout"])
+    if cfg.get("q_len"):
+        lens = st["context_lens"]
+        st = workloads.structure_for_lengths(workloads.CONFIG_IDS[cfg["config"]], lens,
+                                             q_lens=np.full(lens.shape[0], cfg["q_len"], np.int32))
     if cfg.get("only_chunk"):
         s_ = int(np.argmax(st["q_lens"]))
         L = int(st["q_lens"][s_])

@@ -152,3 +152,18 @@ def test_mixed_fp32_chunks_are_unsupported(gpu):
     with pytest.raises(pkv.PkvError) as e:
         dc.mixed(dc.plan(2, mixed=True))
     assert e.value.status == pkv._abi.PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("q_len", [2, 4, 8])
+def test_speculative_verify_rows(gpu, q_len):
+    """Every sequence brings a few new rows at once (a speculative verify
+    step), next to plain decode rows: all of them through the mixed path."""
+    log(f"speculative verify q_len={q_len}")
+    rng = np.random.default_rng(170 + q_len)
+    lens = rng.integers(100, 1500, size=18).astype(np.int32)
+    ql = np.full(18, q_len, np.int32)
+    ql[[3, 11]] = 1
+    case = workloads.build_case(f"spec{q_len}", 170 + q_len, lens.tolist(), ql.tolist(), num_q_heads=32,
+                                num_kv_heads=8, head_dim=128, block_size=16)
+    out, ref, plan = _run(case, gpu)
+    check_close(out, ref, "bf16", f"spec q_len={q_len} units={plan.desc.num_units} merges={plan.desc.num_merges}")
