@@ -28,6 +28,12 @@ Readings of points the pages leave open:
 * ``n == 0`` gives a zero output row and ``lse = -inf``.
 * ``slot < 0`` and slots past the pool are skipped by the write.
 * The fp32 ``scale`` multiplies ``q . k`` before the maximum is taken.
+* Variants ("How Easy Is It to Start Serving LLMs?", Phase 4 §2 names logit
+  soft-capping and sliding windows as template parameters of one kernel
+  family, without formulas).  Read as: a soft-cap ``c > 0`` replaces each
+  scaled logit ``S`` by ``c * tanh(S / c)`` before the softmax; a window
+  ``W > 0`` lets the row at position ``p`` see keys ``p - W < j <= p``
+  (its last ``W`` keys, itself included).  ``0`` turns either off.
 """
 
 from __future__ import annotations
@@ -90,12 +96,14 @@ def gather_kv(cache: np.ndarray, table_row: np.ndarray, n: int) -> np.ndarray:
 
 
 def attention_over_range(qf: np.ndarray, kf: np.ndarray, vf: np.ndarray, positions: np.ndarray,
-                         scale: float, key_begin: int, key_end: int):
+                         scale: float, key_begin: int, key_end: int, soft_cap: float = 0.0, window: int = 0):
     """Exact softmax attention of rows ``qf`` over keys ``[key_begin, key_end)``.
 
     ``qf`` is ``[L, D]`` fp64, ``kf``/``vf`` are ``[n, D]`` fp64 for one kv head,
     ``positions[i]`` is row ``i``'s position; key ``j`` is visible to row ``i``
-    when ``j <= positions[i]``.  Returns ``(o, lse)``: ``o`` ``[L, D]`` is the
+    when ``j <= positions[i]`` (and, with a window ``W > 0``, ``j >
+    positions[i] - W``); a soft-cap ``c > 0`` maps every scaled logit ``S``
+    to ``c * tanh(S / c)``.  Returns ``(o, lse)``: ``o`` ``[L, D]`` is the
     normalised output over the visible keys of the range and ``lse`` ``[L]``
     is ``log(sum_j exp(S_ij))`` (``-inf`` and a zero row when no key of the
     range is visible).
@@ -107,8 +115,13 @@ def attention_over_range(qf: np.ndarray, kf: np.ndarray, vf: np.ndarray, positio
     if key_end <= key_begin:
         return o, lse
     s = np.float64(np.float32(scale)) * (qf @ kf[key_begin:key_end].T)
+    if soft_cap > 0:
+        c = np.float64(np.float32(soft_cap))
+        s = c * np.tanh(s / c)
     keys = np.arange(key_begin, key_end)[None, :]
     visible = keys <= np.asarray(positions)[:, None]
+    if window > 0:
+        visible &= keys > np.asarray(positions)[:, None] - int(window)
     s = np.where(visible, s, -np.inf)
     m = s.max(axis=1)
     has = np.isfinite(m)
@@ -158,12 +171,16 @@ def paged_attention(
     v_scale: float = 1.0,
     seqs=None,
     kv_indptr=None,
+    soft_cap: float = 0.0,
+    window: int = 0,
 ):
     """Exact attention over a paged cache; returns ``(out, lse)`` in fp64.
 
     With ``kv_indptr`` given, ``block_tables`` is the flat ``kv_indices``
     array and sequence ``s`` reads its pages from
     ``kv_indices[kv_indptr[s]:kv_indptr[s+1]]`` (the CSR page table).
+    ``soft_cap`` and ``window`` select the variants described in the module
+    notes (both off at 0).
 
     For every sequence ``s`` (or only those listed in ``seqs``): gather its
     ``n = context_lens[s]`` keys and values through the block table, decode
@@ -211,7 +228,8 @@ def paged_attention(
         pos = n - L + np.arange(L)
         for h in range(hq):
             g = h // group
-            o, l = attention_over_range(qf[r0:r1, h, :], ks[:, g, :], vs[:, g, :], pos, scale, 0, n)
+            o, l = attention_over_range(qf[r0:r1, h, :], ks[:, g, :], vs[:, g, :], pos, scale, 0, n, soft_cap,
+                                        window)
             out[r0:r1, h, :] = o
             lse[r0:r1, h] = l
     return out, lse

@@ -360,3 +360,91 @@ def test_csr_page_table_equals_dense(bs, extra):
     got, got_lse = oracle.paged_attention(q, "f32", kp, vp, "bf16", indices, np.asarray(lens, np.int32), cu, 0.25,
                                           kv_indptr=indptr)
     assert np.array_equal(got, ref) and np.array_equal(got_lse, ref_lse)
+
+
+# --- variants: logit soft-cap and sliding window (readings of Phase 4 §2) ---
+
+def _variant_case(seed, lens, q_lens, hq=4, hkv=2, d=16, bs=4):
+    K, V, _ = _single(lens, hq, hkv, d, bs, seed=seed, kv_dtype="bf16")
+    kp, vp, t = page_out(K, V, bs, perm_seed=seed + 1)
+    rng = np.random.default_rng(seed + 2)
+    q = rng.standard_normal((sum(q_lens), hq, d)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    return q, kp, vp, t, np.asarray(lens, np.int32), cu
+
+
+def _attn(q, kp, vp, t, lens, cu, scale, **kw):
+    return oracle.paged_attention(q, "f32", kp, vp, "bf16", t, lens, cu, scale, **kw)
+
+
+def test_soft_cap_large_cap_is_plain_attention():
+    q, kp, vp, t, lens, cu = _variant_case(20, [37, 100, 5], [1, 4, 2])
+    plain, plain_lse = _attn(q, kp, vp, t, lens, cu, 0.3)
+    capped, capped_lse = _attn(q, kp, vp, t, lens, cu, 0.3, soft_cap=1e7)
+    assert np.allclose(capped, plain, rtol=0, atol=1e-9) and np.allclose(capped_lse, plain_lse, rtol=0, atol=1e-9)
+
+
+def test_soft_cap_equal_scores_give_the_mean_of_v():
+    """Identical keys give identical logits whatever the cap: a plain mean."""
+    rng = np.random.default_rng(21)
+    n, hkv, d = 9, 1, 8
+    k = np.tile(rng.standard_normal((1, hkv, d)).astype(np.float32), (n, 1, 1))
+    v = rng.standard_normal((n, hkv, d)).astype(np.float32)
+    kp, vp, t = page_out([k], [v], 4, perm_seed=3)
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    cu = np.array([0, 1], np.int32)
+    out, _ = oracle.paged_attention(q, "f32", kp, vp, "f32", t, np.array([n], np.int32), cu, 2.0, soft_cap=0.7)
+    assert np.allclose(out[0, 0], v[:, 0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-12)
+
+
+def test_soft_cap_saturation_closed_form():
+    """With the cap fixed and the scale huge, every capped logit is +c or -c
+    (by the sign of q.k), so the output is (e^c sum V+ + e^-c sum V-) /
+    (e^c N+ + e^-c N-)."""
+    rng = np.random.default_rng(22)
+    n, d, c = 12, 8, 1.5
+    k = rng.standard_normal((n, 1, d)).astype(np.float32)
+    v = rng.standard_normal((n, 1, d)).astype(np.float32)
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    kp, vp, t = page_out([k], [v], 4, perm_seed=5)
+    out, _ = oracle.paged_attention(q, "f32", kp, vp, "f32", t, np.array([n], np.int32), np.array([0, 1], np.int32),
+                                    1e9, soft_cap=c)
+    dots = (k[:, 0, :].astype(np.float64) @ q[0, 0].astype(np.float64))
+    pos, neg = dots > 0, dots < 0
+    vv = v[:, 0, :].astype(np.float64)
+    cf = float(np.float32(c))
+    expect = (np.exp(cf) * vv[pos].sum(0) + np.exp(-cf) * vv[neg].sum(0)) / (np.exp(cf) * pos.sum() + np.exp(-cf) * neg.sum())
+    assert np.allclose(out[0, 0], expect, rtol=0, atol=1e-9)
+
+
+def test_window_at_least_the_context_is_plain_attention():
+    q, kp, vp, t, lens, cu = _variant_case(23, [37, 100, 5], [1, 4, 2])
+    plain, _ = _attn(q, kp, vp, t, lens, cu, 0.3)
+    wide, _ = _attn(q, kp, vp, t, lens, cu, 0.3, window=100)
+    assert np.array_equal(plain, wide)
+
+
+def test_window_of_one_returns_the_rows_own_value():
+    q, kp, vp, t, lens, cu = _variant_case(24, [37, 100, 5], [1, 4, 2])
+    out, _ = _attn(q, kp, vp, t, lens, cu, 0.3, window=1)
+    for s in range(3):
+        n, L = int(lens[s]), int(cu[s + 1] - cu[s])
+        vs = nx.bf16_bits_to_f64(oracle.gather_kv(vp, t[s], n))
+        for i in range(L):
+            for h in range(4):
+                assert np.array_equal(out[cu[s] + i, h], vs[n - L + i, h // 2])
+
+
+@pytest.mark.parametrize("w", [2, 7, 30])
+def test_window_equals_attention_over_the_last_keys(w):
+    """A window W is plain attention over the truncated sequence that starts
+    at the first visible key: for a decode row (one row at position n - 1),
+    keys n - W .. n - 1 re-paged as a sequence of their own."""
+    lens = [37, 100, 5]
+    q, kp, vp, t, lens_a, cu = _variant_case(25, lens, [1, 1, 1])
+    got, _ = _attn(q, kp, vp, t, lens_a, cu, 0.3, window=w)
+    K = [oracle.gather_kv(kp, t[s], n)[max(0, n - w):] for s, n in enumerate(lens)]
+    V = [oracle.gather_kv(vp, t[s], n)[max(0, n - w):] for s, n in enumerate(lens)]
+    k2, v2, t2 = page_out(K, V, 4, perm_seed=11)
+    ref, _ = oracle.paged_attention(q, "f32", k2, v2, "bf16", t2, np.array([len(x) for x in K], np.int32), cu, 0.3)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
