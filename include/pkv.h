@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 /* Status codes. */
 #define PKV_OK 0
@@ -114,7 +114,9 @@ typedef struct pkv_plan {
     int32_t max_block_merges; /* most row-block records any plan with these q_lens can have;
                                  these two size the merge launch of a call made while its
                                  stream is being captured */
-    int32_t reserved0;
+    int32_t window_left;      /* sliding window: a row at position p sees keys p - window_left < j <= p
+                                 (0: every key up to p) */
+    float logits_soft_cap;    /* scores pass through c * tanh(s / c) before the softmax (0: off) */
     int64_t off_units;        /* byte offsets inside the workspace */
     int64_t off_queues;
     int64_t off_merges;
@@ -124,7 +126,7 @@ typedef struct pkv_plan {
     int64_t workspace_bytes;  /* bytes of workspace the plan uses */
 } pkv_plan;
 
-#define PKV_PLAN_MAGIC 0x504b5633 /* "PKV3" */
+#define PKV_PLAN_MAGIC 0x504b5634 /* "PKV4" */
 
 /* Text of a status code; never NULL. */
 const char* paged_attn_strerror(int status);
@@ -240,6 +242,32 @@ int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
                              int32_t max_seqs, int32_t max_tokens, void* host_staging, size_t host_staging_bytes,
                              void* workspace, size_t workspace_bytes, pkv_plan* plan, void* stream);
+
+/*
+ * paged_attn_plan_variant - paged_attn_plan_capacity for an attention
+ * variant, which the plan carries to every paged_attn_decode(_csr) /
+ * paged_attn_mixed(_csr) call made with it:
+ *   logits_soft_cap c > 0: every score s = scale * q . k (k_scale folded in)
+ *     becomes c * tanh(s / c) before the softmax (logit soft-capping);
+ *   window_left W > 0: a row at position p sees the keys j with p - W < j <= p
+ *     only (a sliding window of W keys ending at the row), and the planner
+ *     skips the keys that no row of a piece can see.
+ * ("How Easy Is It to Start Serving LLMs?", Phase 4 §2: soft-capping and
+ * sliding windows are among the attention variants one kernel template
+ * serves.  Here both are run-time switches of the same kernels: each costs
+ * a uniform branch per tile, so no extra kernel is built per variant.)
+ * c = 0 and W = 0 give the plain plan.  max_seqs < 0 lays the image out at
+ * the plan's own sizes (as paged_attn_plan); max_seqs >= 0 at the capacity
+ * (as paged_attn_plan_capacity).  workspace == NULL: host only (as
+ * paged_attn_plan_host, host_staging receiving the image, num_queues >= 1).
+ * Errors as those calls, plus PKV_ERR_SHAPE for c < 0, a non-finite c or
+ * W < 0.
+ */
+int paged_attn_plan_variant(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                            float logits_soft_cap, int32_t window_left, int32_t max_seqs, int32_t max_tokens,
+                            void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
+                            pkv_plan* plan, void* stream);
 
 /*
  * paged_attn_decode - one query row per sequence (token s is sequence s).

@@ -44,6 +44,7 @@ EXPORTS = (
     "paged_attn_plan_host",
     "paged_attn_plan",
     "paged_attn_plan_capacity",
+    "paged_attn_plan_variant",
     "paged_attn_decode",
     "paged_attn_mixed",
     "paged_attn_decode_csr",
@@ -71,7 +72,8 @@ class PkvPlan(ctypes.Structure):
         ("num_block_merges", ctypes.c_int32),
         ("max_row_merges", ctypes.c_int32),
         ("max_block_merges", ctypes.c_int32),
-        ("reserved0", ctypes.c_int32),
+        ("window_left", ctypes.c_int32),
+        ("logits_soft_cap", ctypes.c_float),
         ("off_units", ctypes.c_int64),
         ("off_queues", ctypes.c_int64),
         ("off_merges", ctypes.c_int64),
@@ -117,6 +119,9 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_plan_capacity.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp, sz,
                                                P(PkvPlan), vp]
         L.paged_attn_plan_capacity.restype = ctypes.c_int
+        L.paged_attn_plan_variant.argtypes = [vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, sz, vp, sz,
+                                              P(PkvPlan), vp]
+        L.paged_attn_plan_variant.restype = ctypes.c_int
         L.paged_attn_decode.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i64, i32,
                                         f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_decode.restype = ctypes.c_int
@@ -206,18 +211,28 @@ def paged_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale: float 
     _check(st, "paged_kv_write")
 
 
-def plan_host(context_lens, q_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, num_queues: int):
-    """Run the host planner only; returns ``(PkvPlan, image bytes as np.uint8)``."""
+def plan_host(context_lens, q_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, num_queues: int, *,
+              soft_cap: float = 0.0, window: int = 0):
+    """Run the host planner only; returns ``(PkvPlan, image bytes as np.uint8)``.
+    A soft-cap or window plans through ``paged_attn_plan_variant`` (host only)."""
     ctx = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
     ql = None if q_lens is None else np.ascontiguousarray(np.asarray(q_lens, dtype=np.int32))
     p = PkvPlan()
     ql_ptr = None if ql is None else ql.ctypes.data
-    _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], num_q_heads, num_kv_heads, head_dim,
-                                      num_queues, None, 0, ctypes.byref(p)), "paged_attn_plan_host")
+
+    def run(buf, nbytes):
+        if soft_cap != 0.0 or window != 0:
+            _check(lib().paged_attn_plan_variant(ctx.ctypes.data, ql_ptr, ctx.shape[0], num_q_heads, num_kv_heads,
+                                                 head_dim, num_queues, float(soft_cap), int(window), -1, -1, buf,
+                                                 nbytes, None, 0, ctypes.byref(p), None), "paged_attn_plan_variant")
+        else:
+            _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], num_q_heads, num_kv_heads,
+                                              head_dim, num_queues, buf, nbytes, ctypes.byref(p)),
+                   "paged_attn_plan_host")
+
+    run(None, 0)
     image = np.zeros(max(int(p.image_bytes), 1), dtype=np.uint8)
-    _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], num_q_heads, num_kv_heads, head_dim,
-                                      num_queues, image.ctypes.data, image.nbytes, ctypes.byref(p)),
-           "paged_attn_plan_host")
+    run(image.ctypes.data, image.nbytes)
     return p, image
 
 
@@ -259,11 +274,18 @@ class Plan:
     once and never replaced, and the image keeps the same offsets, so attention
     calls captured into a HIP graph (e.g. ``torch.cuda.CUDAGraph``) stay valid
     across updates with the same q_lens.
+
+    ``soft_cap`` (> 0: scores pass through ``c * tanh(s / c)``) and ``window``
+    (> 0: a row at position p sees keys p - window < j <= p) select an
+    attention variant through ``paged_attn_plan_variant``; every attention
+    call made with the plan computes that variant.
     """
 
     def __init__(self, context_lens, q_lens=None, *, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                 device=None, num_queues: int = 0, stream=None, capacity=None):
+                 device=None, num_queues: int = 0, stream=None, capacity=None, soft_cap: float = 0.0,
+                 window: int = 0):
         torch = _torch()
+        self.soft_cap, self.window = float(soft_cap), int(window)
         self.device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
         self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
         with torch.cuda.device(self.device):
@@ -302,7 +324,20 @@ class Plan:
             for attempt in range(2):
                 staging, ws = self._staging[i], self.workspace
                 t1 = time.perf_counter()
-                if self.capacity is not None:
+                variant = self.soft_cap != 0.0 or self.window != 0
+                if variant:
+                    max_seqs, max_tokens = self.capacity if self.capacity is not None else (-1, -1)
+                    st = lib().paged_attn_plan_variant(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                                       self.num_kv_heads, self.head_dim, self.num_queues,
+                                                       self.soft_cap, self.window, max_seqs, max_tokens,
+                                                       staging.data_ptr() if staging is not None else None,
+                                                       staging.numel() if staging is not None else 0,
+                                                       ws.data_ptr() if ws is not None else None,
+                                                       ws.numel() if ws is not None else 0, ctypes.byref(self.desc),
+                                                       st_ptr)
+                    if st == PKV_OK and ws is None:  # a host-only call: no workspace yet
+                        st = PKV_ERR_WORKSPACE
+                elif self.capacity is not None:
                     st = lib().paged_attn_plan_capacity(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
                                                         self.num_kv_heads, self.head_dim, self.num_queues,
                                                         self.capacity[0], self.capacity[1], staging.data_ptr(),
@@ -318,9 +353,15 @@ class Plan:
                 self.last_plan_s = time.perf_counter() - t1
                 if st in (PKV_ERR_WORKSPACE, PKV_ERR_NULL) and attempt == 0 and self.capacity is None:
                     probe = PkvPlan()
-                    _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
-                                                      self.num_kv_heads, self.head_dim, self.num_queues, None, 0,
-                                                      ctypes.byref(probe)), "paged_attn_plan_host")
+                    if variant:
+                        _check(lib().paged_attn_plan_variant(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                                             self.num_kv_heads, self.head_dim, self.num_queues,
+                                                             self.soft_cap, self.window, -1, -1, None, 0, None, 0,
+                                                             ctypes.byref(probe), None), "paged_attn_plan_variant")
+                    else:
+                        _check(lib().paged_attn_plan_host(ctx.ctypes.data, ql_ptr, ctx.shape[0], self.num_q_heads,
+                                                          self.num_kv_heads, self.head_dim, self.num_queues, None, 0,
+                                                          ctypes.byref(probe)), "paged_attn_plan_host")
                     if staging is None or staging.numel() < probe.image_bytes:
                         self._staging[i] = torch.empty(max(int(probe.image_bytes), 256), dtype=torch.uint8,
                                                        pin_memory=True)

@@ -57,7 +57,8 @@ int check_attention(void* out, const void* q, int32_t q_dtype, int64_t q_token_s
         plan->num_wide_merges < 0 || plan->num_block_merges < 0 ||
         plan->num_wide_merges + plan->num_block_merges > plan->num_merges ||
         plan->num_wide_merges > plan->max_row_merges || plan->num_block_merges > plan->max_block_merges ||
-        plan->num_merges - plan->num_block_merges > plan->max_row_merges)
+        plan->num_merges - plan->num_block_merges > plan->max_row_merges || plan->window_left < 0 ||
+        !(plan->logits_soft_cap >= 0.f) || !std::isfinite(plan->logits_soft_cap))
         return PKV_ERR_PLAN;
     if (rows == 0) return PKV_OK;
     if (out == nullptr || q == nullptr || k_cache == nullptr || v_cache == nullptr || block_tables == nullptr ||
@@ -99,6 +100,11 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     a.block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(static_cast<uint32_t>(block_size)) : -1;
     a.qk_scale = scale * (fp8 ? k_scale : 1.f) * kLog2e;
     a.v_scale = fp8 ? v_scale : 1.f;
+    // the soft-cap in the scores' log2 units, and the exponent factor of
+    // tanh(s / c) = 1 - 2 / (e^(2 s / c) + 1) for such scores
+    a.soft_cap = plan->logits_soft_cap > 0.f ? plan->logits_soft_cap * kLog2e : 0.f;
+    a.soft_cap_k = plan->logits_soft_cap > 0.f ? 2.f / plan->logits_soft_cap : 0.f;
+    a.window = plan->window_left;
     a.units = reinterpret_cast<const Unit*>(ws + plan->off_units);
     a.queue_off = reinterpret_cast<const int32_t*>(ws + plan->off_queues);
     a.partial_o = reinterpret_cast<float*>(ws + plan->off_partial_o);
@@ -185,17 +191,26 @@ int paged_attn_plan_host(const int32_t* context_lens_host, const int32_t* q_lens
                      host_image, host_bytes, plan);
 }
 
-int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
-                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
-                    void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
-                    pkv_plan* plan, void* stream) {
-    if (plan == nullptr || host_staging == nullptr || workspace == nullptr) return PKV_ERR_NULL;
+int paged_attn_plan_variant(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                            float logits_soft_cap, int32_t window_left, int32_t max_seqs, int32_t max_tokens,
+                            void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
+                            pkv_plan* plan, void* stream) {
+    if (plan == nullptr) return PKV_ERR_NULL;
+    if (workspace == nullptr) {  // host only
+        return plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
+                         host_staging, host_staging_bytes, plan, max_seqs >= 0 ? max_seqs : -1,
+                         max_seqs >= 0 ? max_tokens : -1, logits_soft_cap, window_left);
+    }
+    if (host_staging == nullptr) return PKV_ERR_NULL;
+    if (max_seqs >= 0 && max_tokens < 0) return PKV_ERR_SHAPE;
     if (num_queues <= 0) {
         const int st = paged_attn_default_queues(&num_queues);
         if (st != PKV_OK) return st;
     }
     int st = plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
-                       host_staging, host_staging_bytes, plan);
+                       host_staging, host_staging_bytes, plan, max_seqs >= 0 ? max_seqs : -1,
+                       max_seqs >= 0 ? max_tokens : -1, logits_soft_cap, window_left);
     if (st != PKV_OK) return st;
     if (workspace_bytes < static_cast<size_t>(plan->workspace_bytes) || !aligned(workspace, kAlign)) {
         plan->magic = 0;
@@ -209,29 +224,25 @@ int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host
     return PKV_OK;
 }
 
+int paged_attn_plan(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
+                    void* host_staging, size_t host_staging_bytes, void* workspace, size_t workspace_bytes,
+                    pkv_plan* plan, void* stream) {
+    if (plan == nullptr || host_staging == nullptr || workspace == nullptr) return PKV_ERR_NULL;
+    return paged_attn_plan_variant(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   num_queues, 0.f, 0, -1, -1, host_staging, host_staging_bytes, workspace,
+                                   workspace_bytes, plan, stream);
+}
+
 int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_lens_host, int32_t num_seqs,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_queues,
                              int32_t max_seqs, int32_t max_tokens, void* host_staging, size_t host_staging_bytes,
                              void* workspace, size_t workspace_bytes, pkv_plan* plan, void* stream) {
     if (plan == nullptr || host_staging == nullptr || workspace == nullptr) return PKV_ERR_NULL;
     if (max_seqs < 0 || max_tokens < 0) return PKV_ERR_SHAPE;
-    if (num_queues <= 0) {
-        const int st = paged_attn_default_queues(&num_queues);
-        if (st != PKV_OK) return st;
-    }
-    int st = plan_host(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim, num_queues,
-                       host_staging, host_staging_bytes, plan, max_seqs, max_tokens);
-    if (st != PKV_OK) return st;
-    if (workspace_bytes < static_cast<size_t>(plan->workspace_bytes) || !aligned(workspace, kAlign)) {
-        plan->magic = 0;
-        return PKV_ERR_WORKSPACE;
-    }
-    if (hipMemcpyAsync(workspace, host_staging, static_cast<size_t>(plan->image_bytes), hipMemcpyHostToDevice,
-                       static_cast<hipStream_t>(stream)) != hipSuccess) {
-        plan->magic = 0;
-        return PKV_ERR_HIP;
-    }
-    return PKV_OK;
+    return paged_attn_plan_variant(context_lens_host, q_lens_host, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                   num_queues, 0.f, 0, max_seqs, max_tokens, host_staging, host_staging_bytes,
+                                   workspace, workspace_bytes, plan, stream);
 }
 
 }  // extern "C"

@@ -25,11 +25,23 @@ struct AttnArgs {
     int32_t block_shift;          // log2(block_size) when a power of two, else -1
     float qk_scale;               // scale * k_scale * log2(e): scores in log2 units
     float v_scale;                // applied to the final output
+    float soft_cap;               // logit soft-cap in log2 units (cap * log2 e), 0: off
+    float soft_cap_k;             // 2 log2(e) / soft_cap: tanh(s / cap) = 1 - 2 / (2^(s * soft_cap_k) + 1)
+    int32_t window;               // keys visible to a row at position p: p - window < j <= p; 0: all
     const Unit* units;
     const int32_t* queue_off;
     float* partial_o;             // [rows][hq][D]
     float* partial_lse;           // [rows][hq], log2 units
 };
+
+// A score s in log2 units under the logit soft-cap c (log2 units too):
+// c * tanh(s / c), with tanh(x) = 1 - 2 / (e^(2x) + 1) and e^(2x) =
+// 2^(s * 2 / c) since s and c carry the same factor log2 e.  Saturates to
+// +-c for large |s| (2^x overflows to inf or underflows to 0).
+__device__ __forceinline__ float soft_cap_log2(float s, float cap, float cap_k) {
+    const float e = exp2_fast(s * cap_k);
+    return cap * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+}
 
 // Index in the block table of the page holding token t, and t's row in it
 // (shifts for a power-of-two page size, else a division).

@@ -222,7 +222,8 @@ constexpr float kRescaleThreshold = 8.0f;
 template <int QDT, int KVDT, int D, int G, int U, int KW, int EPL>
 __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Words<KW> (&v)[U],
                                              const QSlice<QDT, KVDT, D> (&q)[G], float (&acc)[G][EPL],
-                                             float& m_run, float& l_run, float qk_scale, bool my_valid, int col) {
+                                             float& m_run, float& l_run, float qk_scale, float cap, float cap_k,
+                                             bool my_valid, int col) {
     using R = DecodeRegs<QDT, KVDT, D, G>;
     f32x16_t part;  // partial q.k of this lane's slice, index u * G + g
 #pragma unroll
@@ -251,6 +252,7 @@ __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Word
     }
     // lane col now holds the full score of (token 4 (col / G) + row, head col % G)
     float sc = row16_reduce_scatter(part) * qk_scale;
+    if (cap > 0.f) sc = soft_cap_log2(sc, cap, cap_k);  // uniform: a variant of the whole call
     sc = my_valid ? sc : -INFINITY;
     const float mt = row_group_max<G>(sc);
     const bool need = mt > m_run + kRescaleThreshold;
@@ -312,7 +314,7 @@ struct DecodeRun {
     int64_t tok_bytes;
     // the unit
     Unit un;
-    int n, n_dev, kb, ke, h;
+    int n, n_dev, kb, ke, lo, h;  // lo: first key the row sees (its window)
     SeqTable tbl;
     uint32_t head_off, lane_off;
     int64_t clamp_off;
@@ -351,6 +353,7 @@ struct DecodeRun {
         n_dev = as_const(a.context_lens)[u.seq];
         kb = u.kv_begin;
         ke = min(u.kv_end, n);
+        lo = a.window > 0 ? max(0, n - a.window) : 0;
         tbl = seq_table(a, u.seq);
         const char* qbase = static_cast<const char*>(a.q) +
                             (static_cast<int64_t>(u.row0) * a.q_stride + static_cast<int64_t>(h) * G * D +
@@ -411,8 +414,8 @@ struct DecodeRun {
                     tile_pages<U>(pf_pages, a, tbl, pf_t, ke);
                 }
             }
-            process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale,
-                                                      t0 + my_tok < tb, col);
+            process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale, a.soft_cap,
+                                                      a.soft_cap_k, t0 + my_tok < tb && t0 + my_tok >= lo, col);
         }
     }
 
@@ -508,9 +511,10 @@ struct DecodeRun {
     }
 };
 
-// Whether a decode unit covers its sequence's whole key range (its result is
-// the output row).
-__device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.kv_begin == 0 && u.kv_end >= u.pos0 + 1; }
+// Whether a decode unit's result is the output row: it was not cut into
+// pieces, so the plan gave it no partial row.  (A whole unit need not start
+// at key 0: under a sliding window it starts at its first visible tile.)
+__device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.prow < 0; }
 
 // One decode unit, all of it, on the calling workgroup: every kv head, whole
 // units to the output row, pieces to their partial row.

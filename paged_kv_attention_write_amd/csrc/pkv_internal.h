@@ -89,10 +89,12 @@ PlanSections plan_capacity(int64_t max_seqs, int64_t max_tokens, int32_t num_q_h
 
 // Planner (pkv_plan.cpp).  Pure host code.  cap_seqs >= 0 lays the image
 // out at the offsets of plan_capacity(cap_seqs, cap_tokens, ...) instead of
-// the plan's own sizes.
+// the plan's own sizes.  soft_cap and window are recorded in the plan; the
+// window also trims the key ranges.
 int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
-              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs = -1, int32_t cap_tokens = -1);
+              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs = -1, int32_t cap_tokens = -1,
+              float soft_cap = 0.f, int32_t window = 0);
 
 // Upper bounds used by paged_attn_workspace_size.
 void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,

@@ -16,8 +16,14 @@
 // the units fill them about once; a unit's cost is its matrix-core work
 // expressed in tiles, and the units are placed largest first, each whole on
 // the least-loaded prefill queue.
+//
+// With a sliding window of W keys a row at position p sees keys
+// p - W < j <= p only: the ranges above then start at the first tile that
+// holds a key some row of the piece can see, and the work counts only the
+// visible (row, key) pairs.
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <queue>
 #include <vector>
@@ -78,12 +84,14 @@ PlanSections plan_capacity(int64_t max_seqs, int64_t max_tokens, int32_t num_q_h
 
 int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, int32_t num_queues, void* host_image,
-              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs, int32_t cap_tokens) {
+              size_t host_bytes, pkv_plan* plan, int32_t cap_seqs, int32_t cap_tokens, float soft_cap,
+              int32_t window) {
     if (plan == nullptr || (num_seqs > 0 && ctx == nullptr)) return PKV_ERR_NULL;
     std::memset(plan, 0, sizeof(*plan));
     if (num_seqs < 0 || num_queues < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 ||
         num_q_heads % num_kv_heads != 0)
         return PKV_ERR_SHAPE;
+    if (!(soft_cap >= 0.f) || !std::isfinite(soft_cap) || window < 0) return PKV_ERR_SHAPE;
     if (cap_seqs >= 0 && (num_seqs > cap_seqs || cap_tokens < 0)) return PKV_ERR_SHAPE;
 
     // Validate lengths and collect packed row offsets.
@@ -105,13 +113,17 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     const int32_t group = num_q_heads / num_kv_heads;
     const int32_t block_rows = std::max(1, kPrefillQRows / group);
 
+    // first key a row at position p sees, and the first key of the tile
+    // holding it (the start of a range over rows from position p on)
+    auto first_key = [window](int64_t p) { return window > 0 ? std::max<int64_t>(0, p - window + 1) : 0; };
+    auto range_start = [&](int64_t p) { return first_key(p) / kTileTokens * kTileTokens; };
     // visible (row, key) pairs of rows [r0, r1) of a chunk of L rows over n
     // keys, against keys [kb, ke)
-    auto pairs_of = [](int32_t n, int32_t L, int32_t r0, int32_t r1, int64_t kb, int64_t ke) {
+    auto pairs_of = [&](int32_t n, int32_t L, int32_t r0, int32_t r1, int64_t kb, int64_t ke) {
         int64_t pairs = 0;
         for (int32_t r = r0; r < r1; ++r) {
             const int64_t last = static_cast<int64_t>(n) - L + r;  // position of row r
-            pairs += std::max<int64_t>(0, std::min<int64_t>(ke - 1, last) - kb + 1);
+            pairs += std::max<int64_t>(0, std::min<int64_t>(ke - 1, last) - std::max<int64_t>(kb, first_key(last)) + 1);
         }
         return pairs;
     };
@@ -124,7 +136,7 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int32_t n = ctx[s];
         const int32_t L = q_lens ? q_lens[s] : 1;
-        if (L == 1) decode_tiles += ceil_div(n, kTileTokens);
+        if (L == 1) decode_tiles += ceil_div(n - range_start(n - 1), kTileTokens);
         if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
     }
     // Decode rows and prefill chunks run as two launches, each balanced on
@@ -143,25 +155,27 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int32_t r1 = std::min(L, r0 + block_rows);
             const int32_t nr = r1 - r0;
             const int32_t extent = n - L + r1;  // keys the last row of the block sees
+            const int64_t start = range_start(n - L + r0);  // the first row's first tile
+            const int64_t span = extent - start;
             // pieces per kv head: the row block's share of the prefill queues
             // (its work over the chunks' total), so that the chunk units fill
             // the prefill queues about once; at least one, at most
             // kPrefillMaxPieces, none shorter than kPrefillPieceMin keys
-            const int64_t block_flops = pairs_of(n, L, r0, r1, 0, extent) * flops_per_pair * num_kv_heads;
+            const int64_t block_flops = pairs_of(n, L, r0, r1, start, extent) * flops_per_pair * num_kv_heads;
             const int64_t share = static_cast<int64_t>(
                 static_cast<double>(prefill_queues) * static_cast<double>(block_flops) /
                 (static_cast<double>(prefill_flops) * num_kv_heads));
-            const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, extent / kPrefillPieceMin));
+            const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, span / kPrefillPieceMin));
             const int64_t ask = std::min<int64_t>(most, std::max<int64_t>(1, share));
-            const int64_t piece = ceil_div(ceil_div(extent, ask), kTileTokens) * kTileTokens;
-            const int32_t parts = static_cast<int32_t>(ceil_div(extent, piece));  // no empty piece
+            const int64_t piece = ceil_div(ceil_div(span, ask), kTileTokens) * kTileTokens;
+            const int32_t parts = static_cast<int32_t>(ceil_div(span, piece));  // no empty piece
             const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
             if (parts > 1) {
                 merges.push_back(Merge{row0[s] + r0, nr, prow0, parts});
                 partial_rows += static_cast<int64_t>(parts) * nr;
             }
             for (int32_t c = 0; c < parts; ++c) {
-                const int64_t kb = c * piece;
+                const int64_t kb = start + c * piece;
                 const int64_t ke = std::min<int64_t>(extent, kb + piece);
                 const int64_t flops = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
                 const int64_t cost = std::max<int64_t>(1, (flops + kFlopsPerTile / 2) / kFlopsPerTile);
@@ -197,11 +211,15 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     std::vector<int32_t> order;
     for (int32_t s = 0; s < num_seqs; ++s)
         if ((q_lens ? q_lens[s] : 1) == 1 && ctx[s] > 0) order.push_back(s);
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return ctx[a] > ctx[b]; });
+    // keys a decode row reads: from the tile of its first visible key on
+    auto decode_keys = [&](int32_t s) { return ctx[s] - range_start(ctx[s] - 1); };
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return decode_keys(a) > decode_keys(b); });
     std::vector<std::pair<int32_t, size_t>> placed;  // (queue, index) of the pieces of one request
     for (int32_t s : order) {
         const int32_t n = ctx[s];
-        int64_t remaining = ceil_div(n, kTileTokens);
+        const int64_t start = range_start(n - 1);
+        int64_t remaining = ceil_div(n - start, kTileTokens);
         int64_t first = 0;
         placed.clear();
         while (remaining > 0) {
@@ -209,8 +227,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             // never reached while a queue is below the share; kept so that a
             // full lightest queue takes the rest instead of looping
             const int64_t take = target > load ? std::min(remaining, target - load) : remaining;
-            const int32_t kb = static_cast<int32_t>(first * kTileTokens);
-            const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, (first + take) * kTileTokens));
+            const int32_t kb = static_cast<int32_t>(start + first * kTileTokens);
+            const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, start + (first + take) * kTileTokens));
             queues[q].push_back(Unit{s, kb, ke, row0[s], 1, n - 1, -1, kUnitDecode});
             placed.emplace_back(q, queues[q].size() - 1);
             heap.push(load + take, q);
@@ -289,6 +307,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     plan->num_block_merges = num_block;
     plan->max_row_merges = static_cast<int32_t>(row_slots);
     plan->max_block_merges = static_cast<int32_t>(std::min<int64_t>(block_slots, INT32_MAX));
+    plan->window_left = window;
+    plan->logits_soft_cap = soft_cap;
     plan->off_units = 0;
     plan->off_queues = static_cast<int64_t>(units_bytes);
     plan->off_merges = static_cast<int64_t>(units_bytes + queues_bytes);

@@ -206,15 +206,18 @@ struct RingTile {
 // online softmax update, and O^T += V^T P^T.  qk = |scale * k_scale * log2 e|
 // (a negative factor is carried by the sign of q, and qk >= 2^-100).  mask
 // (uniform in the wave): the tile crosses the causal diagonal, the end of the
-// key range or rows past the unit, so keys are tested one by one; otherwise
-// every key of the tile is visible to every pair of the wave.  Per score the
+// key range, a row's window start (a key is visible while pos - key < win)
+// or rows past the unit, so keys are tested one by one; otherwise every key
+// of the tile is visible to every pair of the wave.  cap > 0 (uniform): the
+// scores pass through the logit soft-cap first.  Per score the
 // vector work is one fma into one v_exp_f32, a share of a max tree, a packed
 // bf16 conversion and a dot2 into the row sum.  The first VH blocks of the V
 // operand are read before the softmax so that the reads overlap it.
 template <int D, int VH, class Tile>
-__device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, int pos, bool row_ok, bool mask, int n,
-                                           int g4, float qk, const bf16x8_t (&qb)[D / 32], f32x4_t (&acc)[D / 16],
-                                           float& m_run, float& l_run) {
+__device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, int pos, int win, bool row_ok, bool mask,
+                                           int n, int g4, float qk, float cap, float cap_k,
+                                           const bf16x8_t (&qb)[D / 32], f32x4_t (&acc)[D / 16], float& m_run,
+                                           float& l_run) {
     constexpr int NS = D / 32;
     constexpr int ND = D / 16;
     const uint16_t* const kl = T.k_lane(n, g4);
@@ -229,11 +232,16 @@ __device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[4 * kb2 + i] = c[i];
     }
+    if (cap > 0.f) {  // capped scores are already in log2 units
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sv[j] = soft_cap_log2(sv[j] * qk, cap, cap_k);
+        qk = 1.f;
+    }
     if (mask) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int kp = t0 + 16 * (j >> 2) + 4 * g4 + (j & 3);
-            sv[j] = (row_ok && kp < kend && kp <= pos) ? sv[j] : -INFINITY;
+            sv[j] = (row_ok && kp < kend && kp <= pos && pos - kp < win) ? sv[j] : -INFINITY;
         }
     }
     // V^T operand: lane group g4 takes keys 4 g4 + j (j < 4) and 16 + 4 g4 +
@@ -296,6 +304,7 @@ struct PfWave {
     static constexpr int NS = D / 32;  // k steps of the first product
     static constexpr int ND = D / 16;  // 16-row blocks of O^T
     int n, g4, r, hq_idx, pos, h, kb, kend;
+    int win;  // window: keys pos - win < j <= pos (INT32_MAX: no window)
     bool row_ok, wave_has_rows, wave_full;
     int wave_first_pos, wave_last_pos;
     SeqTable tbl;
@@ -327,6 +336,7 @@ struct PfWave {
         const int n_ctx = as_const(a.context_lens)[un.seq];
         kb = un.kv_begin;
         kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
+        win = a.window > 0 ? a.window : INT32_MAX;
         tbl = seq_table(a, un.seq);
 
         // q slice of this lane's pair: elements 32 s + 8 g4 .. + 7
@@ -356,13 +366,20 @@ struct PfWave {
         bad = false;
     }
 
-    __device__ __forceinline__ bool computes(int t0) const { return wave_has_rows && t0 <= wave_last_pos; }
+    // Tiles wholly past the wave's last row, or wholly before the first
+    // row's window, hold no key any pair of the wave sees.
+    __device__ __forceinline__ bool computes(int t0) const {
+        return wave_has_rows && t0 <= wave_last_pos && wave_first_pos - (t0 + kPfKeys - 1) < win;
+    }
     __device__ __forceinline__ bool masked(int t0) const {
-        return !(wave_full && t0 + kPfKeys <= kend && t0 + kPfKeys - 1 <= wave_first_pos);
+        return !(wave_full && t0 + kPfKeys <= kend && t0 + kPfKeys - 1 <= wave_first_pos &&
+                 wave_last_pos - t0 < win);
     }
     template <int VH, class Tile>
-    __device__ __forceinline__ void tile(const Tile& T, int t0) {
-        if (computes(t0)) pf_compute<D, VH>(T, t0, kend, pos, row_ok, masked(t0), n, g4, qk, qb, acc, m_run, l_run);
+    __device__ __forceinline__ void tile(const AttnArgs& a, const Tile& T, int t0) {
+        if (computes(t0))
+            pf_compute<D, VH>(T, t0, kend, pos, win, row_ok, masked(t0), n, g4, qk, a.soft_cap, a.soft_cap_k, qb, acc,
+                              m_run, l_run);
     }
 
     __device__ __forceinline__ void close(const AttnArgs& a, const Unit& un) {
@@ -436,7 +453,7 @@ __device__ __forceinline__ void prefill_queue(const AttnArgs& a, int queue, Pref
         // (loaded two phases ago) into the other buffer and reloads its
         // register set with tile t + 3.
         auto phase = [&](int t0, int buf, PfRegs<KVDT, D>& rs, int32_t& pg) {
-            W.template tile<D / 32>(PaddedTile<D>{&lds.k[buf][0][0], &lds.v[buf][0][0]}, t0);
+            W.template tile<D / 32>(a, PaddedTile<D>{&lds.k[buf][0][0], &lds.v[buf][0][0]}, t0);
             // unconditional, also past the last tile: the other buffer is
             // free (every wave passed the previous barrier) and every address
             // stays in bounds, so the loads keep one fixed order and their
@@ -587,7 +604,7 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
             ring_barrier();
             if (tt + 3 < ntiles) issue(nxt, t0 + 3 * kPfKeys, use_e);
             load_e = entries(t0 + 5 * kPfKeys);
-            W.template tile<D / 32>(RingTile{cur}, t0);
+            W.template tile<D / 32>(a, RingTile{cur}, t0);
         };
         for (int tt = 0; tt < ntiles; tt += kRingStages) {
             phase(tt, s0, s3, e[3], e[1]);

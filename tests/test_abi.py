@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.pkv_abi_version() == 3
+    assert L.pkv_abi_version() == 4
 
 
 def test_strerror_covers_all_codes():
@@ -160,6 +160,78 @@ def test_mixed_plan_covers_every_visible_pair_once():
             mine = us[us[:, 7] == kind]
             assert sorted(mine[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
         assert len(us) == parts * (hkv if us[0, 7] >= 1 else 1)
+
+
+def _first_key(pos, window):
+    return max(0, pos - window + 1) if window > 0 else 0
+
+
+@pytest.mark.parametrize("window", [1, 16, 100, 700, 5000])
+def test_window_plan_covers_every_visible_pair_once(window):
+    """With a sliding window each (row, key) pair with pos - W < key <= pos is
+    in exactly one unit of its kv head, and a range starts no earlier than the
+    tile that holds its first row's first visible key."""
+    lens, ql = _mixed_case()
+    p, image = pkv.plan_host(lens, ql, 32, 8, 128, 96, window=window)
+    assert p.window_left == window and p.logits_soft_cap == 0.0
+    units, qoff, merges = pkv.decode_plan_image(p, image)
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    hkv = 8
+    for s in range(len(lens)):
+        n, L = int(lens[s]), int(ql[s])
+        heads = hkv if L > 1 else 1
+        cover = np.zeros((heads, L, n), np.int32)
+        mine = units[units[:, 0] == s]
+        for u in mine:
+            seq, kb, ke, row0, nrows, pos0, prow, kind = (int(x) for x in u)
+            assert kb < ke
+            r = row0 - cu[s]
+            assert kb >= _first_key(pos0, window) // 16 * 16
+            for i in range(nrows):
+                pos = pos0 + i
+                lo, hi = max(kb, _first_key(pos, window)), min(ke, pos + 1)
+                if hi > lo:
+                    cover[max(kind - 1, 0), r + i, lo:hi] += 1
+        pos = n - L + np.arange(L)
+        j = np.arange(n)[None, :]
+        visible = (j <= pos[:, None]) & (j > pos[:, None] - window)
+        assert np.array_equal(cover, np.broadcast_to(visible.astype(np.int32), cover.shape)), s
+        # the first piece of each row block starts at its first row's tile
+        for row0 in set(mine[:, 3].tolist()):
+            blk = mine[mine[:, 3] == row0]
+            assert blk[:, 1].min() == _first_key(int(blk[0, 5]), window) // 16 * 16
+    _check_wide_first(p, merges, ql)
+
+
+def test_variant_plan_without_variant_equals_the_plain_plan():
+    lens, ql = _mixed_case()
+    p0, img0 = pkv.plan_host(lens, ql, 32, 8, 128, 96)
+    # a soft-cap changes no range; a window at least as long as every context
+    # sees every key
+    for kw in (dict(soft_cap=30.0), dict(window=int(lens.max())), dict(window=10**6, soft_cap=50.0)):
+        p1, img1 = pkv.plan_host(lens, ql, 32, 8, 128, 96, **kw)
+        assert np.array_equal(img0, img1), kw
+        assert p1.num_units == p0.num_units and p1.workspace_bytes == p0.workspace_bytes
+        assert p1.window_left == kw.get("window", 0)
+        assert p1.logits_soft_cap == np.float32(kw.get("soft_cap", 0.0))
+
+
+def test_variant_plan_rejects_bad_variants():
+    for kw in (dict(window=-1), dict(soft_cap=-1.0), dict(soft_cap=float("nan")), dict(soft_cap=float("inf"))):
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.plan_host([50, 9], None, 8, 2, 64, 4, **kw)
+        assert e.value.status == _abi.PKV_ERR_SHAPE, kw
+
+
+def test_window_shrinks_decode_work():
+    """Long decode rows under a window read only the last W keys (rounded
+    down to a tile): the share per queue follows the windowed work."""
+    lens = np.full(64, 8192, np.int32)
+    p, image = pkv.plan_host(lens, None, 32, 8, 128, 256, window=1000)
+    units, _, _ = pkv.decode_plan_image(p, image)
+    keys = int((units[:, 2] - units[:, 1]).sum())
+    assert keys == 64 * (8192 - (8192 - 1000) // 16 * 16)
+    assert p.target_tiles == -(-keys // 16 // 256)
 
 
 def test_mixed_plan_decode_queues_equal_the_decode_plan():
