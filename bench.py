@@ -128,7 +128,7 @@ def fill_fp8(torch, pkv, layers, st, dev):
     return scales
 
 
-def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
+def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0, soft_cap=0.0, window=0):
     """The fp64 oracle on layer 0 (write + attention), repeated up to ~budget_s."""
     import oracle
     from workloads import byte_model
@@ -150,15 +150,15 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0):
     while True:
         k2, v2 = oracle.kv_write(kc, vc, kv_dtype, kn, vn, "bf16", st["slot_mapping"], ks, vs)
         out, _ = oracle.paged_attention(q, "bf16", k2, v2, kv_dtype, st["block_tables"], st["context_lens"], cu,
-                                        scale, ks, vs)
+                                        scale, ks, vs, soft_cap=soft_cap, window=window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     per = el / reps
     kvb = 1 if kv_dtype == "fp8" else 2
-    nbytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2) + \
-        byte_model.write_bytes(T, 8, 128, 2, kvb)
+    nbytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2,
+                                        window=window) + byte_model.write_bytes(T, 8, 128, 2, kvb)
     try:
         from threadpoolctl import threadpool_info
 
@@ -375,6 +375,10 @@ def main():
                     help="time the step only as eager launches (by default the step is also captured once as a "
                          "HIP graph of every layer's write + attention, the plan made for a fixed capacity, and "
                          "replayed after each step's re-plan; value and ms_per_step then come from the replays)")
+    ap.add_argument("--soft-cap", type=float, default=0.0,
+                    help="attention variant: logit soft-cap c (scores through c * tanh(s / c)); 0: off")
+    ap.add_argument("--window", type=int, default=0,
+                    help="attention variant: sliding window of W keys (a row at p sees p - W < j <= p); 0: off")
     ap.add_argument("--study", choices=["skew", "plan-cost", "pages"],
                     help="instead of the bench line: the load-balance study over length mixes (skew) or the "
                          "planner cost over batch sizes (plan-cost), one JSON line per case")
@@ -435,15 +439,17 @@ def main():
     cu = torch.from_numpy(st["cu_seqlens"]).to(dev)
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
     q_lens = st["q_lens"] if mixed else None
+    variant = dict(soft_cap=args.soft_cap, window=args.window)
     plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
-                    num_queues=args.queues)
+                    num_queues=args.queues, **variant)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
 
-    attn_bytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2)
-    attn_flops = byte_model.attention_flops(st["context_lens"], st["q_lens"], 32, 128)
+    attn_bytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], kvb, 2,
+                                            window=args.window)
     chunk = st["q_lens"] > 1
-    chunk_flops = byte_model.attention_flops(st["context_lens"][chunk], st["q_lens"][chunk], 32, 128)
+    chunk_flops = byte_model.attention_flops(st["context_lens"][chunk], st["q_lens"][chunk], 32, 128,
+                                             window=args.window)
     wr_bytes = byte_model.write_bytes(T, 8, 128, 2, kvb)
     step_bytes = args.layers * (attn_bytes + wr_bytes)
 
@@ -491,7 +497,7 @@ def main():
         # layer) with a plan of fixed capacity; each timed step re-plans into
         # that plan's workspace, then replays it
         plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
-                        num_queues=args.queues, capacity=(B, T))
+                        num_queues=args.queues, capacity=(B, T), **variant)
 
         def layers_only():
             for l, layer in enumerate(layers):
@@ -548,6 +554,8 @@ def main():
         roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                              "chunk_tflops": round(mfma_tflops, 2)}
 
+    variant_desc = "".join([f", soft-cap {args.soft_cap:g}" if args.soft_cap else "",
+                            f", window {args.window}" if args.window else ""])
     result = {
         "metric": METRIC,
         "value": round(value, 4),
@@ -562,7 +570,8 @@ def main():
         "dtype": kv_dtype,
         "data": "synthetic: seeded N(0,1) K/V/Q, seeded lengths and shuffled block tables",
         "config": {
-            "workload": f"{args.config}: {cfg['desc']}; one step = plan + {args.layers} layers x (write + attention)",
+            "workload": f"{args.config}: {cfg['desc']}{variant_desc}; one step = plan + {args.layers} layers x "
+                        f"(write + attention)",
             "num_seqs": int(B),
             "query_rows": int(T),
             "total_context_tokens": int(st["context_lens"].sum()),
@@ -584,13 +593,13 @@ def main():
     }
     if graph_info is not None:
         result["graph"] = graph_info
-    rec = recorded_traffic(args.config)
+    rec = recorded_traffic(args.config) if not variant_desc else None
     if rec is not None:
         result["roofline"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])
         result["roofline"]["traffic_source"] = rec["profile"]
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cb = cpu_baseline(torch, st, layers[0], kv_dtype, scales[0], args.cpu_budget)
+        cb = cpu_baseline(torch, st, layers[0], kv_dtype, scales[0], args.cpu_budget, **variant)
         # parity of layer 0's last timed output against the oracle run above
         got = layers[0]["out"].float().cpu().numpy().astype(np.float64)
         cb_out = cb.pop("out")

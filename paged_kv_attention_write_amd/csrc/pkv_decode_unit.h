@@ -219,7 +219,7 @@ constexpr float kRescaleThreshold = 8.0f;
 
 // One wave-tile of the online softmax: scores of the 4U tokens x G heads,
 // lazy rescale, P V accumulate.
-template <int QDT, int KVDT, int D, int G, int U, int KW, int EPL>
+template <int QDT, int KVDT, int D, int G, int U, int KW, int EPL, bool CAP>
 __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Words<KW> (&v)[U],
                                              const QSlice<QDT, KVDT, D> (&q)[G], float (&acc)[G][EPL],
                                              float& m_run, float& l_run, float qk_scale, float cap, float cap_k,
@@ -252,7 +252,7 @@ __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Word
     }
     // lane col now holds the full score of (token 4 (col / G) + row, head col % G)
     float sc = row16_reduce_scatter(part) * qk_scale;
-    if (cap > 0.f) sc = soft_cap_log2(sc, cap, cap_k);  // uniform: a variant of the whole call
+    if constexpr (CAP) sc = soft_cap_log2(sc, cap, cap_k);
     sc = my_valid ? sc : -INFINITY;
     const float mt = row_group_max<G>(sc);
     const bool need = mt > m_run + kRescaleThreshold;
@@ -396,6 +396,10 @@ struct DecodeRun {
             }
         }
         pf_t = -1;
+        const uint32_t vspan = static_cast<uint32_t>(max(tb - lo, 0));  // keys lo .. tb - 1 are valid
+        // the loop is built twice, with and without the logit soft-cap, so
+        // that the plain call's loop carries no test of it
+        auto loop = [&](auto cap_on) {
         for (int t0 = ta + sub * TT; t0 < tb; t0 += step) {
             Words<KW> kr[U], vr[U];
             if constexpr (!UNIFORM_PAGE) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
@@ -414,8 +418,17 @@ struct DecodeRun {
                     tile_pages<U>(pf_pages, a, tbl, pf_t, ke);
                 }
             }
-            process_tile<QDT, KVDT, D, G, U, KW, EPL>(kr, vr, q, acc, m_run, l_run, a.qk_scale, a.soft_cap,
-                                                      a.soft_cap_k, t0 + my_tok < tb && t0 + my_tok >= lo, col);
+            // lo <= t0 + my_tok < tb as one unsigned compare
+            const bool valid = static_cast<uint32_t>(t0 - lo + my_tok) < vspan;
+            process_tile<QDT, KVDT, D, G, U, KW, EPL, decltype(cap_on)::value>(kr, vr, q, acc, m_run, l_run,
+                                                                               a.qk_scale, a.soft_cap, a.soft_cap_k,
+                                                                               valid, col);
+        }
+        };
+        if (a.soft_cap > 0.f) {
+            loop(std::true_type{});
+        } else {
+            loop(std::false_type{});
         }
     }
 
