@@ -32,7 +32,7 @@ constexpr int64_t kFlopsPerTile = 13000000;
 // Alignment of the sections of the workspace.
 // A one-row merge record with at least this many pieces is "wide": its
 // merge gives every q head a workgroup whose waves split the pieces.
-constexpr int kWideMergeParts = 4;
+constexpr int kWideMergeParts = 8;
 
 constexpr size_t kAlign = 256;
 

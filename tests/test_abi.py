@@ -93,10 +93,10 @@ def test_plan_partials_and_merges_are_consistent():
 
 
 def _check_wide_first(p, merges, q_lens=None, group=4):
-    """Merge records come as wide ones (one row, at least 4 pieces), then row
+    """Merge records come as wide ones (one row, at least 8 pieces), then row
     blocks, then one-row records with few pieces, counted in the plan; the
     room bounds follow from q_lens alone."""
-    kind = np.where(merges[:, 1] > 1, 1, np.where(merges[:, 3] >= 4, 0, 2))
+    kind = np.where(merges[:, 1] > 1, 1, np.where(merges[:, 3] >= 8, 0, 2))
     assert np.all(np.diff(kind) >= 0)
     assert int(p.num_wide_merges) == int((kind == 0).sum())
     assert int(p.num_block_merges) == int((kind == 1).sum())
