@@ -254,8 +254,10 @@ int paged_attn_plan_capacity(const int32_t* context_lens_host, const int32_t* q_
  *     skips the keys that no row of a piece can see.
  * ("How Easy Is It to Start Serving LLMs?", Phase 4 §2: soft-capping and
  * sliding windows are among the attention variants one kernel template
- * serves.  Here both are run-time switches of the same kernels: each costs
- * a uniform branch per tile, so no extra kernel is built per variant.)
+ * serves.  Here both are run-time switches of the same kernels: the decode
+ * tile loop is built with and without the cap, the window is one more term
+ * of each key's validity test, and the prefill tile takes both as uniform
+ * branches.)
  * c = 0 and W = 0 give the plain plan.  max_seqs < 0 lays the image out at
  * the plan's own sizes (as paged_attn_plan); max_seqs >= 0 at the capacity
  * (as paged_attn_plan_capacity).  workspace == NULL: host only (as
@@ -277,7 +279,8 @@ int paged_attn_plan_variant(const int32_t* context_lens_host, const int32_t* q_l
  *   keys of sequence s, K_s[j] = k_cache[block_tables[s][j / block_size]]
  *   [j % block_size].  An FP8 cache is read as code * k_scale (K) and
  *   code * v_scale (V).  Arithmetic in fp32; out has q's dtype (round to
- *   nearest even).
+ *   nearest even).  A plan from paged_attn_plan_variant applies its
+ *   soft-cap to every scaled score and restricts j to its window.
  * ("nanoserve", Triton paged-attention decode bullet: every decode reads K/V
  * straight from the block table with an online softmax; "How Easy Is It to
  * Start Serving LLMs?", Phase 4 §1 and §3.)
@@ -286,7 +289,8 @@ int paged_attn_plan_variant(const int32_t* context_lens_host, const int32_t* q_l
  *   q_token_stride    elements between tokens of q (>= num_q_heads * head_dim)
  *   kv_dtype          F32 (q F32), BF16 (q BF16), FP8_E4M3 (q BF16)
  *   head_dim          64 or 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}
- *   plan, workspace   from paged_attn_plan with q_lens NULL (or all ones)
+ *   plan, workspace   from paged_attn_plan (or _capacity, _variant) with q_lens NULL
+ *                     (or all ones)
  * Errors: PKV_ERR_NULL, PKV_ERR_DTYPE, PKV_ERR_UNSUPPORTED, PKV_ERR_SHAPE,
  * PKV_ERR_PLAN (plan made for other shapes or a mixed batch),
  * PKV_ERR_WORKSPACE, PKV_ERR_HIP.
