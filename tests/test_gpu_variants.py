@@ -17,7 +17,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import DeviceCase, as_f64, check_close, log, oracle_caches
+from gpu_helpers import DeviceCase, as_f64, check_close, log, oracle_caches, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -163,3 +163,66 @@ def test_no_variant_is_the_plain_call(gpu):
     wide = dc.mixed(_plan(case, gpu, True, 0.0, 10 ** 6, 17))
     torch.cuda.synchronize()
     assert torch.equal(plain.view(torch.int16), wide.view(torch.int16))
+
+
+def test_variants_through_csr_tables(gpu):
+    """The CSR entry points with a variant plan give the dense calls' bits."""
+    import torch
+    import paged_kv_attention_write_amd as pkv
+
+    log("variants through CSR tables")
+    case = workloads.build_case("vcsr", 197, MIXED_LENS, MIXED_Q, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                block_size=16, scale=0.3)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    plan = _plan(case, gpu, True, 11.0, 250, 17)
+    dense = dc.mixed(plan)
+    rows = [case.block_tables[s, :-(-int(n) // 16)] for s, n in enumerate(case.context_lens)]
+    indptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    indices = np.concatenate(rows).astype(np.int32)
+    out = torch.empty_like(dc.q)
+    pkv.paged_attn_mixed_csr(out, dc.q, dc.kc, dc.vc, to_dev(indptr, gpu), to_dev(indices, gpu), dc.cu, dc.ctx,
+                             case.scale, plan, case.k_scale, case.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), dense.view(torch.int16))
+
+
+def test_variant_decode_in_a_graph(gpu):
+    """A decode call with a soft-cap and window plan of fixed capacity,
+    captured once and replayed after re-plans of the same lengths, with
+    eager work between replays: every replay equals the eager call."""
+    import torch
+    import paged_kv_attention_write_amd as pkv
+
+    log("variant decode in a graph")
+    case = workloads.build_case("vgr", 198, DECODE_LENS, [1] * len(DECODE_LENS), num_q_heads=32, num_kv_heads=8,
+                                head_dim=128, block_size=16, scale=0.4)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    B = len(DECODE_LENS)
+    plan = _plan(case, gpu, False, 20.0, 700, 0, capacity=(B, B))
+    eager = dc.decode(plan).clone()
+    out = torch.empty_like(dc.q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dc.decode(plan, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dc.decode(plan, out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.zero_()
+        plan.update(case.context_lens)
+        g.replay()
+        x = torch.randn(1 << 20, device=gpu)
+        float((x * 2.0).sum())
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle.paged_attention(case.q, case.q_dtype, kr, vr, case.kv_dtype, case.block_tables,
+                                    case.context_lens, case.cu_seqlens, case.scale, case.k_scale, case.v_scale,
+                                    soft_cap=20.0, window=700)
+    check_close(as_f64(out), ref, "bf16", "graph decode cap 20 W 700")
