@@ -87,6 +87,55 @@ __device__ __forceinline__ void merge_fold(MergeState<D / 64>& st, const float* 
     }
 }
 
+// The row-block and few-piece records fold with every lane taking 4
+// consecutive elements of one (row, q head), one 16-byte load per part: a
+// wave covers 256 / D heads, a workgroup kMergeWaves times that.
+template <int D>
+constexpr int kMergeHeadsPerWave = 256 / D;
+
+// Fold all parts of row r of a record for the lane's 4 elements of q head h
+// (h clamped into range for the loads; the caller drops lanes past hq), in
+// the same order and arithmetic as merge_fold.
+template <int D>
+__device__ __forceinline__ void merge_fold4(float& M, float& sw, float (&acc)[4], bool& nan,
+                                            const float* __restrict__ po, const float* __restrict__ pl, int hq,
+                                            int prow0, int nrows, int parts, int r, int h, int e0) {
+    constexpr int B = kMergeBatch;
+    const int64_t hd = static_cast<int64_t>(hq) * D;
+    for (int cb = 0; cb < parts; cb += B) {
+        float l[B];
+        float4 x[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int64_t prow = prow0 + static_cast<int64_t>(min(cb + b, parts - 1)) * nrows + r;
+            l[b] = pl[prow * hq + h];
+            x[b] = *reinterpret_cast<const float4*>(po + prow * hd + static_cast<int64_t>(h) * D + e0);
+        }
+        float mb = M;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (cb + b >= parts) l[b] = -INFINITY;  // a repeated last part counts once
+            nan |= l[b] != l[b];
+            mb = fmaxf(mb, l[b]);
+        }
+        if (mb == -INFINITY) continue;  // every part so far is empty
+        const float f = exp2_fast(M - mb);  // 0 while M is -inf
+        sw *= f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= f;
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float w = exp2_fast(l[b] - mb);  // 0 for an empty part
+            sw += w;
+            acc[0] = fmaf(w, x[b].x, acc[0]);
+            acc[1] = fmaf(w, x[b].y, acc[1]);
+            acc[2] = fmaf(w, x[b].z, acc[2]);
+            acc[3] = fmaf(w, x[b].w, acc[3]);
+        }
+        M = mb;
+    }
+}
+
 template <int QDT, int D>
 __device__ __forceinline__ void merge_store(void* __restrict__ out, int64_t oi, const float (&acc)[D / 64], float sw,
                                             bool nan, float v_scale) {
@@ -112,8 +161,9 @@ __device__ __forceinline__ void merge_store(void* __restrict__ out, int64_t oi, 
 //    through LDS (each scaled by 2^(m_w - M), an empty wave adding nothing);
 //  - row blocks of chunk rows, then one-row records with few pieces: the
 //    next block_slots * max_rows * hgroups blocks and the last
-//    row_slots * hgroups blocks give each (record, row, group of kMergeWaves q
-//    heads) a workgroup, one wave per head folding all of its parts.
+//    row_slots * hgroups blocks give each (record, row, group of
+//    kMergeWaves * kMergeHeadsPerWave<D> q heads) a workgroup, every lane
+//    folding all parts of 4 elements of one head.
 // The live numbers of records come from `counts` in the workspace when it is
 // given (a launch sized for what any plan with these q_lens can hold, made
 // once and replayed for later plans), else from the arguments; blocks past
@@ -178,7 +228,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
                             nan, v_scale);
         return;
     }
-    const int hgroups = (hq + kMergeWaves - 1) / kMergeWaves;
+    constexpr int HPW = kMergeHeadsPerWave<D>;
+    constexpr int LPH = 64 / HPW;  // lanes per head
+    const int hgroups = (hq + kMergeWaves * HPW - 1) / (kMergeWaves * HPW);
     const int b2 = b - wide_blocks;
     const int block_blocks = block_slots * max_rows * hgroups;
     int rec, r;
@@ -191,14 +243,23 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
         if (rec >= num_merges) return;
         r = 0;
     }
-    const int h = (b2 % hgroups) * kMergeWaves + wave;
+    const int h = (b2 % hgroups) * kMergeWaves * HPW + wave * HPW + lane / LPH;
+    const int e0 = (lane % LPH) * 4;
     const const_ptr<int32_t> mw = reinterpret_cast<const_ptr<int32_t>>(as_const(merges) + rec);
     const int row0 = mw[0], nrows = mw[1], prow0 = mw[2], parts = mw[3];
-    if (h >= hq || r >= nrows) return;
-    MergeState<E> st;
-    merge_fold<D>(st, po, lse, hq, prow0, nrows, parts, r, h, 0, 1, lane);
-    merge_store<QDT, D>(out, static_cast<int64_t>(row0 + r) * hd + static_cast<int64_t>(h) * D + lane * E, st.acc,
-                        st.sw, st.nan, v_scale);
+    if (r >= nrows) return;
+    float M = -INFINITY, sw = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    bool nan = false;
+    merge_fold4<D>(M, sw, acc, nan, po, pl, hq, prow0, nrows, parts, r, min(h, hq - 1), e0);
+    if (h >= hq) return;
+    const float scale = sw > 0.f ? v_scale / sw : 0.f;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = nan ? NAN : acc[e] * scale;
+    store_out<QDT, 4>(static_cast<char*>(out) +
+                          (static_cast<int64_t>(row0 + r) * hd + static_cast<int64_t>(h) * D + e0) * dt_bytes(QDT),
+                      o);
 }
 
 // Launch shape: one persistent workgroup per queue.  8 waves (one per kv head
@@ -288,7 +349,9 @@ int launch_merge(const AttnArgs& a, const pkv_plan* plan, const void* workspace,
         block_slots = plan->max_block_merges;
         row_slots = plan->max_row_merges;
     }
-    const int64_t hgroups = (a.hq + kMergeWaves - 1) / kMergeWaves;
+    const int64_t hpg = static_cast<int64_t>(kMergeWaves) * (head_dim == 64 ? kMergeHeadsPerWave<64>
+                                                                              : kMergeHeadsPerWave<128>);
+    const int64_t hgroups = (a.hq + hpg - 1) / hpg;
     const int64_t blocks = wide_slots * a.hq + block_slots * max_rows * hgroups + row_slots * hgroups;
     if (blocks == 0) return PKV_OK;
     if (blocks > 0x7FFFFFFF) return PKV_ERR_SHAPE;

@@ -218,7 +218,9 @@ __device__ __forceinline__ int64_t clamp_offset(const AttnArgs& a, const SeqTabl
 constexpr float kRescaleThreshold = 8.0f;
 
 // One wave-tile of the online softmax: scores of the 4U tokens x G heads,
-// lazy rescale, P V accumulate.
+// lazy rescale, P V accumulate.  CAP: the scores pass through the logit
+// soft-cap (cap, cap_k in log2 units, see soft_cap_log2) before the mask.
+// my_valid: this lane's token is one the row sees.
 template <int QDT, int KVDT, int D, int G, int U, int KW, int EPL, bool CAP>
 __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Words<KW> (&v)[U],
                                              const QSlice<QDT, KVDT, D> (&q)[G], float (&acc)[G][EPL],
