@@ -158,13 +158,18 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int64_t start = range_start(n - L + r0);  // the first row's first tile
             const int64_t span = extent - start;
             // pieces per kv head: the row block's share of the prefill queues
-            // (its work over the chunks' total), so that the chunk units fill
-            // the prefill queues about once; at least one, at most
-            // kPrefillMaxPieces, none shorter than kPrefillPieceMin keys
+            // (its work over the chunks' total, rounded to the nearest
+            // count), so that the chunk units fill the prefill queues about
+            // once; at least one, at most kPrefillMaxPieces, none shorter than
+            // kPrefillPieceMin keys.  A row block that fills under half a
+            // unit's pairs (a few speculative rows, say) costs little to cut,
+            // having few partial rows, so it is cut 3x finer and the
+            // least-loaded placement packs the pieces evenly.
             const int64_t block_flops = pairs_of(n, L, r0, r1, start, extent) * flops_per_pair * num_kv_heads;
-            const int64_t share = static_cast<int64_t>(
-                static_cast<double>(prefill_queues) * static_cast<double>(block_flops) /
-                (static_cast<double>(prefill_flops) * num_kv_heads));
+            const int64_t fine = static_cast<int64_t>(nr) * group * 2 < kPrefillQRows ? 3 : 1;
+            const int64_t share = static_cast<int64_t>(std::llround(
+                static_cast<double>(fine * prefill_queues) * static_cast<double>(block_flops) /
+                (static_cast<double>(prefill_flops) * num_kv_heads)));
             const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, span / kPrefillPieceMin));
             const int64_t ask = std::min<int64_t>(most, std::max<int64_t>(1, share));
             const int64_t piece = ceil_div(ceil_div(span, ask), kTileTokens) * kTileTokens;

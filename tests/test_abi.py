@@ -363,3 +363,31 @@ def test_decode_argument_checks():
     assert _decode(p, plan=ctypes.byref(stale)) == _abi.PKV_ERR_PLAN
     pm, _ = pkv.plan_host([100, 200, 300, 400], [1, 1, 1, 50], 32, 8, 128, 16)
     assert _decode(pm, B=4) == _abi.PKV_ERR_PLAN                  # a mixed plan is not a decode plan
+
+
+def _prefill_queue_costs(lens, ql, nq=256):
+    p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
+    units, qoff, _ = pkv.decode_plan_image(p, image)
+    Q, P = p.num_queues, p.num_prefill_queues
+
+    def pairs(u):
+        seq, kb, ke, row0, nrows, pos0 = (int(x) for x in u[:6])
+        return sum(max(0, min(ke - 1, pos0 + r) - kb + 1) for r in range(nrows))
+
+    return np.array([sum(pairs(u) for u in units[qoff[q]:qoff[q + 1]]) for q in range(Q, Q + P)])
+
+
+def test_prefill_units_are_balanced():
+    """The prefill queues' visible (row, key) pairs stay within 20 % of their
+    mean for a 512-row chunk over 2560 keys and for 64 sequences of 4
+    speculative rows over U[512, 4096] keys: chunk row blocks are cut to the
+    nearest count of queue shares, and small row blocks 3x finer."""
+    import workloads
+
+    st = workloads.structure_only("mixed", "page16")
+    chunk = st["q_lens"] > 1
+    c = _prefill_queue_costs(st["context_lens"][chunk], st["q_lens"][chunk])
+    assert c.max() <= 1.2 * c.mean(), c.max() / c.mean()
+    lens = workloads.structure_only("decode", "page16")["context_lens"]
+    c = _prefill_queue_costs(lens, np.full(lens.shape[0], 4, np.int32))
+    assert c.max() <= 1.2 * c.mean(), c.max() / c.mean()
