@@ -24,10 +24,6 @@ constexpr int kPrefillPieceMin = 512;
 // Prefill queues per decode queue: the prefill kernel runs two 8-wave
 // workgroups per CU when the decode launch runs one.
 constexpr int kPrefillQueuesPerQueue = 2;
-// Cost of a prefill unit in decode tiles: one tile of decode work (16 keys of
-// 8 kv heads x 128 dims in bf16, 64 KiB) takes a queue about as long as this
-// many flops of matrix-core work.
-constexpr int64_t kFlopsPerTile = 13000000;
 
 // Alignment of the sections of the workspace.
 // A one-row merge record with at least this many pieces is "wide": its

@@ -13,9 +13,9 @@
 // unit per (row block, kv head, key piece), and run as a launch of their own
 // over a second set of queues: the key range of a row block is cut into as
 // many pieces as its share of the chunks' work is of those queues, so that
-// the units fill them about once; a unit's cost is its matrix-core work
-// expressed in tiles, and the units are placed largest first, each whole on
-// the least-loaded prefill queue.
+// the units fill them about once; a unit's cost is its matrix-core flops,
+// and the units are placed largest first, each whole on the least-loaded
+// prefill queue.
 //
 // With a sliding window of W keys a row at position p sees keys
 // p - W < j <= p only: the ranges above then start at the first tile that
@@ -55,7 +55,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct PrefillPiece {
     Unit unit;
-    int64_t cost;   // tiles
+    int64_t cost;   // flops of the unit's visible (row, key) pairs
     int32_t order;  // creation order, breaks cost ties
 };
 
@@ -182,8 +182,7 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             for (int32_t c = 0; c < parts; ++c) {
                 const int64_t kb = start + c * piece;
                 const int64_t ke = std::min<int64_t>(extent, kb + piece);
-                const int64_t flops = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
-                const int64_t cost = std::max<int64_t>(1, (flops + kFlopsPerTile / 2) / kFlopsPerTile);
+                const int64_t cost = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
                 for (int32_t h = 0; h < num_kv_heads; ++h) {
                     const Unit u{s, static_cast<int32_t>(kb), static_cast<int32_t>(ke), row0[s] + r0, nr,
                                  n - L + r0, parts > 1 ? prow0 + c * nr : -1, kUnitPrefill + h};

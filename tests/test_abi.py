@@ -378,16 +378,17 @@ def _prefill_queue_costs(lens, ql, nq=256):
 
 
 def test_prefill_units_are_balanced():
-    """The prefill queues' visible (row, key) pairs stay within 20 % of their
-    mean for a 512-row chunk over 2560 keys and for 64 sequences of 4
-    speculative rows over U[512, 4096] keys: chunk row blocks are cut to the
-    nearest count of queue shares, and small row blocks 3x finer."""
+    """The prefill queues' visible (row, key) pairs stay within 15 % of their
+    mean for a 512-row chunk over 2560 keys, and within 10 % for 64
+    sequences of 4 speculative rows over U[512, 4096] keys: chunk row blocks
+    are cut to the nearest count of queue shares, small row blocks 3x finer,
+    and the units are placed largest first by their exact flops."""
     import workloads
 
     st = workloads.structure_only("mixed", "page16")
     chunk = st["q_lens"] > 1
     c = _prefill_queue_costs(st["context_lens"][chunk], st["q_lens"][chunk])
-    assert c.max() <= 1.2 * c.mean(), c.max() / c.mean()
+    assert c.max() <= 1.15 * c.mean(), c.max() / c.mean()
     lens = workloads.structure_only("decode", "page16")["context_lens"]
     c = _prefill_queue_costs(lens, np.full(lens.shape[0], 4, np.int32))
-    assert c.max() <= 1.2 * c.mean(), c.max() / c.mean()
+    assert c.max() <= 1.1 * c.mean(), c.max() / c.mean()
