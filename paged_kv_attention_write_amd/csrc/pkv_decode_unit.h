@@ -35,7 +35,9 @@ struct DecodeRegs {
     static constexpr int EPL = D / 16;                           // elements per lane
     static constexpr int KW = EPL * dt_bytes(KVDT) / 4;          // K/V words per lane
     static constexpr int QW = EPL * dt_bytes(QDT) / 4;           // q words per lane
-    static constexpr bool kDot2 = (QDT == PKV_DTYPE_BF16 && KVDT == PKV_DTYPE_BF16);
+    // bf16 q against bf16 or fp8 keys: q . k in bf16 pairs (an fp8 key is
+    // exactly a bf16 value)
+    static constexpr bool kDot2 = QDT == PKV_DTYPE_BF16 && (KVDT == PKV_DTYPE_BF16 || KVDT == PKV_DTYPE_FP8_E4M3);
 };
 
 // Query slice of one head held by a lane: bf16 pairs (dot2 path) or fp32.
@@ -87,6 +89,20 @@ __device__ __forceinline__ void kv_to_f32(float (&x)[EPL], const Words<KW>& r) {
             x[4 * w + 2] = hi.x;
             x[4 * w + 3] = hi.y;
         }
+    }
+}
+
+// Key elements 2j and 2j + 1 of a lane's slice as a bf16 pair.  fp8 E4M3
+// values (3 mantissa bits, magnitudes 2^-9 .. 448) are bf16 values exactly:
+// converted to fp32, their low 16 bits are zero.
+template <int KVDT, int KW>
+__device__ __forceinline__ uint32_t key_pair(const Words<KW>& r, int j) {
+    if constexpr (KVDT == PKV_DTYPE_BF16) {
+        return r.w[j];
+    } else {
+        const int w = static_cast<int>(r.w[j >> 1]);
+        const float2_t f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        return (__float_as_uint(f.y) & 0xffff0000u) | (__float_as_uint(f.x) >> 16);
     }
 }
 
@@ -231,13 +247,16 @@ __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Word
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if constexpr (R::kDot2) {
+            uint32_t kp[EPL / 2];
+#pragma unroll
+            for (int j = 0; j < EPL / 2; ++j) kp[j] = key_pair<KVDT, KW>(k[u], j);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float d = 0.f;
 #pragma unroll
                 for (int j = 0; j < EPL / 2; ++j)
                     d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[g].w[j]),
-                                                        __builtin_bit_cast(bf16x2_t, k[u].w[j]), d, false);
+                                                        __builtin_bit_cast(bf16x2_t, kp[j]), d, false);
                 part[u * G + g] = d;
             }
         } else {
