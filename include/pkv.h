@@ -16,11 +16,11 @@
  *
  * Sources (the pages this library follows):
  *   "nanoserve" (README): the paged KV cache and per-request block table; the
- *     packed [T] token batch; one engine step, in which every layer first
- *     writes this step's K/V through per-token cache slots and then attends
- *     over the full context through the block table; the paged decode kernel
- *     with an online softmax over the block table; the split of a mixed step
- *     into decode rows and prefill chunks.
+ *     packed [T] token batch; the engine step, where each layer stores the
+ *     new tokens' K/V by slot before its attention reads the whole context
+ *     through the block table; the paged decode kernel with a running
+ *     softmax; the split of a mixed step into decode rows and prefill
+ *     chunks.
  *   "How to design an LLM serving system (a vLLM deep dive)", section
  *     "PagedAttention": block table, slot_mapping, default block size 16;
  *     "Two phases and the KV cache": kv bytes per token.
@@ -281,9 +281,10 @@ int paged_attn_plan_variant(const int32_t* context_lens_host, const int32_t* q_l
  *   code * v_scale (V).  Arithmetic in fp32; out has q's dtype (round to
  *   nearest even).  A plan from paged_attn_plan_variant applies its
  *   soft-cap to every scaled score and restricts j to its window.
- * ("nanoserve", Triton paged-attention decode bullet: every decode reads K/V
- * straight from the block table with an online softmax; "How Easy Is It to
- * Start Serving LLMs?", Phase 4 §1 and §3.)
+ * ("nanoserve", Triton paged-attention decode bullet: the decode kernel
+ * gathers no K/V into a padded copy but walks the block table itself, with
+ * a running softmax; "How Easy Is It to Start Serving LLMs?", Phase 4 §1 and
+ * §3.)
  *
  *   out, q            device, q_dtype (F32 or BF16), [num_seqs][num_q_heads][head_dim]
  *   q_token_stride    elements between tokens of q (>= num_q_heads * head_dim)
