@@ -241,7 +241,7 @@ template <int QDT, int KVDT, int D, int G, int U, int KW, int EPL, bool CAP>
 __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Words<KW> (&v)[U],
                                              const QSlice<QDT, KVDT, D> (&q)[G], float (&acc)[G][EPL],
                                              float& m_run, float& l_run, float qk_scale, float cap, float cap_k,
-                                             bool my_valid, int col) {
+                                             bool my_valid) {
     using R = DecodeRegs<QDT, KVDT, D, G>;
     f32x16_t part;  // partial q.k of this lane's slice, index u * G + g
 #pragma unroll
@@ -443,7 +443,7 @@ struct DecodeRun {
             const bool valid = static_cast<uint32_t>(t0 - lo + my_tok) < vspan;
             process_tile<QDT, KVDT, D, G, U, KW, EPL, decltype(cap_on)::value>(kr, vr, q, acc, m_run, l_run,
                                                                                a.qk_scale, a.soft_cap, a.soft_cap_k,
-                                                                               valid, col);
+                                                                               valid);
         }
         };
         if (a.soft_cap > 0.f) {
