@@ -9,7 +9,7 @@ kernel, header, helper, table or constant generator.  The only code both
 sides are fed from is the seeded input generator in ``workloads/``, which holds
 no arithmetic of the method.
 
-Sources (the four pages this build follows):
+Sources (the four pages this library follows):
 
 * "How Easy Is It to Start Serving LLMs?" (Geodesic blog), section
   "Phase 4: inside FlashInfer": §1 block-sparse KV memory (the page table in

@@ -33,7 +33,7 @@ def test_printed_numbers():
 
 
 def test_decode_workload_bytes_and_mixed_flops():
-    # 147,456 tokens x 4096 B is the survey's round figure; check the formula's parts
+    # 147,456 tokens x 4096 B is the decode workload's nominal size; check the formula's parts
     lens = np.full(64, 2304)
     b = bm.attention_bytes(lens, np.ones(64), 32, 8, 128, 16, 2, 2)
     kv = 64 * 2304 * 4096
