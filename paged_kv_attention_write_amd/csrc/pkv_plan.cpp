@@ -53,10 +53,11 @@ struct QueueHeap {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A prefill unit and its cost; equal costs keep their creation order (the
+// sort is stable).
 struct PrefillPiece {
     Unit unit;
-    int64_t cost;   // flops of the unit's visible (row, key) pairs
-    int32_t order;  // creation order, breaks cost ties
+    int64_t cost;  // flops of the unit's visible (row, key) pairs
 };
 
 }  // namespace
@@ -186,7 +187,7 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
                 for (int32_t h = 0; h < num_kv_heads; ++h) {
                     const Unit u{s, static_cast<int32_t>(kb), static_cast<int32_t>(ke), row0[s] + r0, nr,
                                  n - L + r0, parts > 1 ? prow0 + c * nr : -1, kUnitPrefill + h};
-                    prefill.push_back(PrefillPiece{u, cost, static_cast<int32_t>(prefill.size())});
+                    prefill.push_back(PrefillPiece{u, cost});
                 }
             }
         }
