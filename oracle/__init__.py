@@ -29,7 +29,8 @@ Modules:
   format definitions.
 * :mod:`oracle.paged_attention` - the KV write, the gather, exact softmax
   attention (fp64), partial attention over a key range and the LSE merge.
-* :mod:`oracle.plan` - the split-KV planner as the blog's §3 describes it.
+* :mod:`oracle.plan` - the split-KV planner as the blog's §3 describes it
+  (the reading the library follows, and the illustration's steps as printed).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_*.py`` against closed forms, brute force,
@@ -51,7 +52,7 @@ from .paged_attention import (
     attention_over_range,
     lse_merge,
 )
-from .plan import split_kv_plan, split_lengths
+from .plan import illustration_plan, split_kv_plan, split_lengths
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -66,5 +67,6 @@ __all__ = [
     "attention_over_range",
     "lse_merge",
     "split_kv_plan",
+    "illustration_plan",
     "split_lengths",
 ]

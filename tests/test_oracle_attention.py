@@ -43,27 +43,36 @@ def _val(x, dtype):
     return x.astype(np.float64) if dtype == "f32" else nx.bf16_bits_to_f64(x)
 
 
-def brute_force(q_rows, K, V, n, scale, hq, hkv):
-    """softmax(scale * q K^T) V with plain loops; q_rows[i][h][d], K[j][g][d]."""
+def brute_force(q_rows, K, V, n, scale, hq, hkv, soft_cap=0.0, window=0):
+    """softmax(scale * q K^T) V with plain loops; q_rows[i][h][d], K[j][g][d].
+
+    Only the keys a row sees are visited at all: keys 0 .. pos, and with a
+    window W > 0 only the last W of them (pos - W < j <= pos).  With a cap
+    c > 0 each visited key's scaled score s becomes c * tanh(s / c)."""
     L = len(q_rows)
     g_size = hq // hkv
     d = len(K[0][0]) if n else len(q_rows[0][0])
     out = []
     for i in range(L):
         pos = n - L + i
+        first = max(0, pos - window + 1) if window > 0 else 0
+        keys = range(first, pos + 1)
         row = []
         for h in range(hq):
             g = h // g_size
             scores = []
-            for j in range(pos + 1):
+            for j in keys:
                 acc = 0.0
                 for e in range(d):
                     acc += q_rows[i][h][e] * K[j][g][e]
-                scores.append(scale * acc)
+                sc = scale * acc
+                if soft_cap > 0:
+                    sc = soft_cap * math.tanh(sc / soft_cap)
+                scores.append(sc)
             m = max(scores)
             w = [math.exp(s - m) for s in scores]
             tot = sum(w)
-            row.append([sum(w[j] * V[j][g][e] for j in range(pos + 1)) / tot for e in range(d)])
+            row.append([sum(w[k] * V[j][g][e] for k, j in enumerate(keys)) / tot for e in range(d)])
         out.append(row)
     return np.array(out)
 
@@ -448,3 +457,30 @@ def test_window_equals_attention_over_the_last_keys(w):
     k2, v2, t2 = page_out(K, V, 4, perm_seed=11)
     ref, _ = oracle.paged_attention(q, "f32", k2, v2, "bf16", t2, np.array([len(x) for x in K], np.int32), cu, 0.3)
     assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("soft_cap,window", [(2.0, 0), (0.0, 5), (2.0, 5), (0.75, 3), (2.0, 1)])
+@pytest.mark.parametrize("bs", [1, 4])
+def test_soft_cap_and_window_match_brute_force_on_causal_chunks(soft_cap, window, bs):
+    """Multi-row causal chunks with 1 < W < n and a moderate cap, against the
+    brute force that never visits a key its row cannot see: a cap applied to
+    masked keys (which would then carry weight e^(-c - m)) or a window off by
+    one fails here, unlike with decode rows or a cap large enough that -c
+    underflows."""
+    rng = np.random.default_rng(700 + bs + int(10 * soft_cap) + window)
+    lens, q_lens = [6, 13, 9, 20], [1, 6, 9, 7]
+    hq, hkv, d = 4, 2, 8
+    K, V = _rand_logical(rng, lens, hkv, d)
+    kp, vp, tables = page_out(K, V, bs, perm_seed=bs + 1, extra_blocks=2)
+    q = (2.0 * rng.standard_normal((sum(q_lens), hq, d))).astype(np.float32)
+    scale = 0.5
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    out, _ = oracle.paged_attention(q, "f32", kp, vp, "f32", tables, np.asarray(lens, np.int32), cu, scale,
+                                    soft_cap=soft_cap, window=window)
+    c64 = float(np.float32(soft_cap))
+    r = 0
+    for s, (n, L) in enumerate(zip(lens, q_lens)):
+        ref = brute_force(q[r:r + L].astype(np.float64).tolist(), K[s].astype(np.float64).tolist(),
+                          V[s].astype(np.float64).tolist(), n, 0.5, hq, hkv, soft_cap=c64, window=window)
+        np.testing.assert_allclose(out[r:r + L], ref, rtol=0, atol=1e-12)
+        r += L

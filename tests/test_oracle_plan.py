@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle.plan import split_kv_plan, split_lengths, TILE_TOKENS
+from oracle.plan import illustration_plan, split_kv_plan, split_lengths, TILE_TOKENS
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -115,3 +115,71 @@ def test_empty_and_zero_lengths():
     assert sum(len(x) for x in q) == 1 and q[0] == [(1, 0, 5)]
     with pytest.raises(ValueError):
         split_kv_plan([3], 0)
+
+
+def _illustration_golden():
+    cases = {}
+    with open(os.path.join(GOLDEN, "plan_illustration_example.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            head, row = line.split("|")
+            ex, lens, nq, tile = head.split()
+            key = (int(ex), tuple(int(x) for x in lens.split(",")), int(nq), int(tile))
+            cases.setdefault(key, []).append(tuple(int(x) for x in row.split()))
+    return cases
+
+
+def test_illustration_worked_examples():
+    """The illustration's steps as printed (cut every request, then place
+    each chunk on the least-loaded queue), against hand-derived placements."""
+    cases = _illustration_golden()
+    assert len(cases) == 3
+    for (_, lens, nq, tile), rows in cases.items():
+        queues = illustration_plan(list(lens), nq, tile)
+        got = [(q, r, b, e) for q, items in enumerate(queues) for (r, b, e) in items]
+        assert got == rows, (lens, nq, tile)
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("nq", [1, 7, 64])
+def test_illustration_covers_once_with_chunks_of_the_target(seed, nq):
+    rng = np.random.default_rng(50 + seed)
+    lens = [int(x) for x in rng.integers(0, 3000, size=int(rng.integers(1, 60)))]
+    queues = illustration_plan(lens, nq)
+    target = sum(lens) / nq
+    chunk = max(1, int(target // 1))
+    spans = {r: [] for r in range(len(lens))}
+    for items in queues:
+        for r, b, e in items:
+            assert 0 <= b < e <= lens[r] and e - b <= chunk
+            spans[r].append((b, e))
+    for r, sp in spans.items():
+        sp.sort()
+        # every chunk but the last is exactly `chunk` long and they tile [0, n)
+        assert [b for b, _ in sp] == list(range(0, lens[r], chunk))
+        assert (sp[-1][1] if sp else 0) == lens[r]
+
+
+def test_queue_balance_of_the_two_readings_on_the_decode_workload():
+    """Largest over mean queue work on the 64-request decode workload
+    (context U[512, 4096]) at 256 queues: cutting every request into
+    target-sized chunks before placing them (the illustration's steps) leaves
+    the largest queue at 1.61x the mean; cutting each piece to what the
+    least-loaded queue can still take leaves it at 1.02x.  These are the
+    figures quoted for the planner reading the library follows."""
+    import workloads
+
+    lens = [int(x) for x in workloads.decode_lengths("decode")]
+    assert len(lens) == 64
+
+    def ratio(queues, tile):
+        loads = [sum(-(-(e - b) // tile) for _, b, e in q) for q in queues]
+        return max(loads) / (sum(loads) / len(loads))
+
+    printed = ratio(illustration_plan(lens, 256), 1)
+    printed_tiles = ratio(illustration_plan(lens, 256, TILE_TOKENS), TILE_TOKENS)
+    lazy = ratio(split_kv_plan(lens, 256), TILE_TOKENS)
+    assert round(printed, 2) == 1.61 and round(printed_tiles, 2) == 1.62
+    assert round(lazy, 2) == 1.02
