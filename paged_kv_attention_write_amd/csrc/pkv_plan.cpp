@@ -146,7 +146,10 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
 
     // Prefill units: row blocks x kv heads x key pieces of every chunk.
     std::vector<PrefillPiece> prefill;
-    std::vector<Merge> merges;
+    // merge records with their kind: 0 wide (one decode row, many pieces),
+    // 1 a block of chunk rows (whatever its row count: a chunk's last block
+    // may hold a single row), 2 the other decode rows
+    std::vector<std::pair<int32_t, Merge>> merges;
     int64_t partial_rows = 0;
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int32_t n = ctx[s];
@@ -177,7 +180,7 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int32_t parts = static_cast<int32_t>(ceil_div(span, piece));  // no empty piece
             const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
             if (parts > 1) {
-                merges.push_back(Merge{row0[s] + r0, nr, prow0, parts});
+                merges.emplace_back(1, Merge{row0[s] + r0, nr, prow0, parts});
                 partial_rows += static_cast<int64_t>(parts) * nr;
             }
             for (int32_t c = 0; c < parts; ++c) {
@@ -244,20 +247,20 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int32_t prow0 = static_cast<int32_t>(partial_rows);
             for (size_t c = 0; c < placed.size(); ++c)
                 queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c);
-            merges.push_back(Merge{row0[s], 1, prow0, static_cast<int32_t>(placed.size())});
+            const int32_t parts = static_cast<int32_t>(placed.size());
+            merges.emplace_back(parts >= kWideMergeParts ? 0 : 2, Merge{row0[s], 1, prow0, parts});
             partial_rows += static_cast<int64_t>(placed.size());
         }
     }
 
-    // merge records: wide ones (one row, many pieces), then row blocks, then
-    // the other one-row records, each kind in its order
-    auto kind = [](const Merge& m) { return m.nrows > 1 ? 1 : (m.parts >= kWideMergeParts ? 0 : 2); };
+    // merge records: wide ones, then row blocks, then the other one-row
+    // records, each kind in its order
     std::stable_sort(merges.begin(), merges.end(),
-                     [&](const Merge& x, const Merge& y) { return kind(x) < kind(y); });
+                     [](const auto& x, const auto& y) { return x.first < y.first; });
     int32_t num_wide = 0, num_block = 0;
     for (const auto& m : merges) {
-        num_wide += kind(m) == 0 ? 1 : 0;
-        num_block += kind(m) == 1 ? 1 : 0;
+        num_wide += m.first == 0 ? 1 : 0;
+        num_block += m.first == 1 ? 1 : 0;
     }
     // records any plan with these q_lens can have: one per decode row, one
     // per block of chunk rows
@@ -345,8 +348,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     counts[0] = static_cast<int32_t>(merges.size());
     counts[1] = num_wide;
     counts[2] = num_block;
-    if (!merges.empty())
-        std::memcpy(base + units_bytes + queues_bytes, merges.data(), merges.size() * sizeof(Merge));
+    Merge* mrec = reinterpret_cast<Merge*>(base + units_bytes + queues_bytes);
+    for (size_t i = 0; i < merges.size(); ++i) mrec[i] = merges[i].second;
     plan->magic = PKV_PLAN_MAGIC;
     return PKV_OK;
 }

@@ -96,17 +96,12 @@ def _check_wide_first(p, merges, q_lens=None, group=4):
     """Merge records come as wide ones (one row, at least 8 pieces), then row
     blocks, then one-row records with few pieces, counted in the plan; the
     room bounds follow from q_lens alone."""
-    kind = np.where(merges[:, 1] > 1, 1, np.where(merges[:, 3] >= 8, 0, 2))
+    from test_plan_random import check_merge_room, merge_kinds
+
+    ql = np.ones(p.num_seqs, np.int64) if q_lens is None else np.asarray(q_lens)
+    kind = merge_kinds(merges, ql)
     assert np.all(np.diff(kind) >= 0)
-    assert int(p.num_wide_merges) == int((kind == 0).sum())
-    assert int(p.num_block_merges) == int((kind == 1).sum())
-    if q_lens is not None:
-        ql = np.asarray(q_lens)
-        assert int(p.max_row_merges) == int((ql == 1).sum())
-        rows = max(1, 128 // group)
-        assert int(p.max_block_merges) == int(sum(-(-int(L) // rows) for L in ql if L > 1))
-    assert int(p.num_wide_merges) <= int(p.max_row_merges)
-    assert int(p.num_block_merges) <= int(p.max_block_merges)
+    check_merge_room(p, merges, ql, group)
 
 
 @pytest.mark.parametrize("mix", ["uniform", "one-long", "heavy"])

@@ -23,6 +23,36 @@ import paged_kv_attention_write_amd as pkv
 from paged_kv_attention_write_amd import _abi
 
 
+def merge_kinds(merges, q_lens):
+    """Kind of each merge record by where it comes from: 1 for a block of
+    chunk rows (even one of a single row), else 0 for a decode row with at
+    least 8 pieces and 2 for one with fewer."""
+    ql = np.asarray(q_lens, np.int64)
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    seq = np.searchsorted(cu, merges[:, 0], side="right") - 1
+    chunk = ql[seq] > 1 if len(merges) else np.zeros(0, bool)
+    return np.where(chunk, 1, np.where(merges[:, 3] >= 8, 0, 2))
+
+
+def check_merge_room(p, merges, q_lens, group):
+    """The counts the attention calls check before launching (and that size
+    a merge launch made under stream capture) hold for the plan the planner
+    made: one-row records fit the room of the decode rows, row-block records
+    the room of the chunks' row blocks."""
+    ql = np.asarray(q_lens, np.int64)
+    kind = merge_kinds(merges, ql)
+    assert int(p.num_merges) == len(merges)
+    assert int(p.num_wide_merges) == int((kind == 0).sum())
+    assert int(p.num_block_merges) == int((kind == 1).sum())
+    rows = max(1, 128 // group)
+    assert int(p.max_row_merges) == int((ql == 1).sum())
+    assert int(p.max_block_merges) == int(sum(-(-int(L) // rows) for L in ql if L > 1))
+    assert p.num_wide_merges + p.num_block_merges <= p.num_merges
+    assert p.num_wide_merges <= p.max_row_merges
+    assert p.num_block_merges <= p.max_block_merges
+    assert p.num_merges - p.num_block_merges <= p.max_row_merges
+
+
 def _random_batch(rng):
     B = int(rng.integers(1, 40))
     lens = rng.integers(0, 6000, size=B)
@@ -47,7 +77,7 @@ def _capacity_plan(lens, ql, hq, hkv, d, nq, window, cap_seqs, cap_tokens):
     return p, image
 
 
-def _check_plan(p, image, lens, ql, hkv, window):
+def _check_plan(p, image, lens, ql, hq, hkv, window):
     units, qoff, merges = pkv.decode_plan_image(p, image)
     cu = np.concatenate([[0], np.cumsum(ql)])
     assert p.num_tokens == cu[-1] and p.num_units == len(units)
@@ -59,8 +89,9 @@ def _check_plan(p, image, lens, ql, hkv, window):
     q32 = np.asarray(image[p.off_queues:p.off_merges]).view(np.int32)
     ci = 3 * nq + 1
     assert list(q32[ci:ci + 3]) == [p.num_merges, p.num_wide_merges, p.num_block_merges]
-    kind = np.where(merges[:, 1] > 1, 1, np.where(merges[:, 3] >= 8, 0, 2))
+    kind = merge_kinds(merges, ql)
     assert np.all(np.diff(kind) >= 0)
+    check_merge_room(p, merges, ql, hq // hkv)
     # merge records and partial rows
     owner = {}
     for m, (row0, nrows, prow0, parts) in enumerate(merges):
@@ -113,7 +144,7 @@ def test_random_batches(seed):
     window = int(rng.choice([0, 0, 1, 17, 300, 5000]))
     p, image = pkv.plan_host(lens, ql, hq, hkv, d, nq, window=window)
     assert p.window_left == window
-    _check_plan(p, image, lens, ql, hkv, window)
+    _check_plan(p, image, lens, ql, hq, hkv, window)
 
     # the same batch at a capacity: same content at the capacity's offsets
     cap_seqs = lens.shape[0] + int(rng.integers(0, 8))
@@ -126,3 +157,17 @@ def test_random_batches(seed):
     assert pkv.lib().paged_attn_workspace_size(cap_seqs, cap_tokens, hq, d, nq, ctypes.byref(ws),
                                                ctypes.byref(host)) == 0
     assert pc.workspace_bytes <= ws.value and pc.image_bytes <= host.value
+
+
+@pytest.mark.parametrize("lens,ql,nq", [([4000], [33], 256), ([4000, 3000], [33, 1], 256), ([4000], [65], 256),
+                                        ([9000, 100], [97, 1], 64), ([2048 + 33], [33], 1024)])
+def test_single_row_chunk_block_is_a_block_record(lens, ql, nq):
+    """A chunk whose last row block holds one row (q_len = 1 mod 128 / G) over
+    a long prefix is cut into pieces; its merge record is a row-block record,
+    so the plan passes the attention calls' room checks."""
+    lens, ql = np.array(lens, np.int32), np.array(ql, np.int32)
+    p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
+    _, _, merges = pkv.decode_plan_image(p, image)
+    assert p.num_block_merges >= 1
+    check_merge_room(p, merges, ql, 4)
+    _check_plan(p, image, lens, ql, 32, 8, 0)
