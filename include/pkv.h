@@ -52,9 +52,11 @@
  *     sits at position n - L + i and sees keys 0 .. n - L + i.
  *   - Device-side contents are trusted except where stated: a block id
  *     outside [0, num_blocks) is never dereferenced; the rows of a sequence
- *     whose table holds one come out as NaN.  Decode rows take their key
- *     ranges from the plan; a decode row whose context_lens entry differs
- *     from the length the plan was made from (a stale plan) comes out as NaN.
+ *     whose table holds one come out as NaN.  Every unit of work takes its
+ *     key range and rows from the plan; a sequence whose context_lens entry
+ *     (or, in a packed batch, whose cu_seqlens entries) differ from what the
+ *     plan was made from (a stale plan) gets NaN in the rows the plan gives
+ *     it.
  *   - Calls that share a workspace must be ordered on one stream.
  */
 #ifndef PKV_H_
@@ -171,6 +173,12 @@ int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int6
  * host staging image for any plan over at most max_seqs sequences and
  * max_tokens query rows with the given query heads, head_dim and queues.
  * num_queues <= 0 asks for the current device's default (a HIP query).
+ * ("How Easy Is It to Start Serving LLMs?", Phase 4 §3: the plan lives in a
+ * GPU buffer of fixed size that every layer of the step reuses, so that the
+ * step can be captured once and replayed; this bounds that buffer.)
+ *   workspace_bytes, host_bytes   out (host); either may be NULL, not both
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (negative sizes, no heads), PKV_ERR_HIP
+ * (the device query failed).
  */
 int paged_attn_workspace_size(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
                               int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes);
@@ -307,12 +315,20 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
  * paged_attn_mixed - a packed batch: sequence s owns query rows
  * cu_seqlens[s] .. cu_seqlens[s+1]-1 of q and out (num_tokens rows in all);
  * row i of its L rows attends causally to keys 0 .. n - L + i of its
- * n = context_lens[s] keys.  Two launches on `stream`: the decode kernel
- * for the rows of one-row sequences (the plan's decode queues) and a tiled
- * kernel for the chunks (its prefill queues), whose QK^T and PV products run
- * on the matrix cores with P rounded to bf16; then one merge of cut pieces.
+ * n = context_lens[s] keys.  cu_seqlens (device int32 [num_seqs + 1]) must
+ * be the exclusive prefix sums of the q_lens the plan was made from; the
+ * rows of a sequence whose entries differ come out as NaN.  The rows of
+ * one-row sequences run the decode unit (the plan's decode queues), the
+ * chunks a tiled unit (its prefill queues) whose QK^T and PV products run on
+ * the matrix cores with P rounded to bf16; then one merge of cut pieces.
+ * With bf16 K/V on pages of a multiple of 16 tokens and 2 or 4 q heads per
+ * kv head, both kinds of unit run in one launch (decode and prefill
+ * workgroups side by side on every compute unit); otherwise the decode and
+ * the prefill units are two launches.  So one call is one or two attention
+ * launches followed by the merge launch.
  * Same arguments and errors as paged_attn_decode, with the plan made from
- * the same q_lens, plus: PKV_ERR_UNSUPPORTED when the plan has chunk rows
+ * the same q_lens, plus: PKV_ERR_NULL for a NULL cu_seqlens with rows to
+ * compute, PKV_ERR_UNSUPPORTED when the plan has chunk rows
  * and q is not bf16 (K/V bf16 or fp8; decode-only plans take every dtype
  * paged_attn_decode takes), PKV_ERR_SHAPE when chunk rows meet a cache not
  * aligned to 8 elements.  A block id outside the pool turns the rows of

@@ -32,7 +32,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 
-PLAN_MAGIC = 0x504B5632
+PLAN_MAGIC = 0x504B5634  # "PKV4", PKV_PLAN_MAGIC in include/pkv.h
 
 # Symbols include/pkv.h declares (checked by the CPU tests).
 EXPORTS = (

@@ -93,6 +93,7 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     a.max_blocks = max_blocks;
     a.kv_indptr = nullptr;
     a.context_lens = context_lens;
+    a.cu_seqlens = nullptr;
     a.hq = hq;
     a.hkv = hkv;
     a.num_blocks = num_blocks;
@@ -150,7 +151,7 @@ int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int6
         return PKV_ERR_SHAPE;
     if (num_tokens == 0) return PKV_OK;
     if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_ERR_NULL;
-    const size_t in_align = new_dtype == PKV_DTYPE_F32 ? 16 : 16;
+    const size_t in_align = 16;
     const size_t out_align = cache_dtype == PKV_DTYPE_FP8_E4M3 ? 8 : 16;
     if (!aligned(k_new, in_align) || !aligned(v_new, in_align) || !aligned(k_cache, out_align) ||
         !aligned(v_cache, out_align))
@@ -323,6 +324,7 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
                            context_lens, num_q_heads, num_kv_heads, num_blocks, block_size, scale, k_scale, v_scale,
                            plan, workspace);
     a.kv_indptr = kv_indptr;
+    a.cu_seqlens = cu_seqlens;
     const int group = num_q_heads / num_kv_heads;
     const bool chunks = plan->num_prefill_units > 0;
     if (chunks && !prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;

@@ -18,6 +18,7 @@ struct AttnArgs {
     int32_t max_blocks;
     const int32_t* kv_indptr;     // [B + 1] CSR row offsets into block_tables, or null (dense rows)
     const int32_t* context_lens;  // [B]
+    const int32_t* cu_seqlens;    // [B + 1] packed row offsets (mixed calls), or null (decode: row s is sequence s)
     int32_t hq;
     int32_t hkv;
     int64_t num_blocks;
@@ -72,6 +73,22 @@ __device__ __forceinline__ SeqTable seq_table(const AttnArgs& a, int seq) {
         return n > 0 ? SeqTable{as_const(a.block_tables) + b, n} : SeqTable{ip, 0};
     }
     return SeqTable{as_const(a.block_tables) + static_cast<int64_t>(seq) * a.max_blocks, a.max_blocks};
+}
+
+// Whether the device-side lengths and row offsets of a unit's sequence
+// disagree with what the plan was made from (a stale plan, or cu_seqlens
+// that are not the prefix sums of the plan's q_lens).  The unit's rows r =
+// 0 .. nrows-1 sit at packed rows row0 + r and positions pos0 + r: with the
+// device's n keys and L = cu[s+1] - cu[s] rows, row row0 + r is row row0 +
+// r - cu[s] of the sequence and sits at n - L + row0 + r - cu[s].  Decode
+// calls (no cu_seqlens) have row s = sequence s and one row each.
+__device__ __forceinline__ bool unit_is_stale(const AttnArgs& a, const Unit& u) {
+    const int32_t n = as_const(a.context_lens)[u.seq];
+    if (a.cu_seqlens == nullptr) return n != u.pos0 + 1;
+    const const_ptr<int32_t> cu = as_const(a.cu_seqlens);
+    const int32_t c0 = cu[u.seq], c1 = cu[u.seq + 1];
+    const int32_t r0 = u.row0 - c0;  // the unit's first row within the sequence
+    return r0 < 0 || r0 + u.nrows > c1 - c0 || u.pos0 != n - (c1 - c0) + r0;
 }
 
 __device__ __forceinline__ Unit load_unit(const_ptr<Unit> units, int i) {

@@ -207,8 +207,8 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
             const uint64_t slot = static_cast<uint64_t>(page) * static_cast<uint32_t>(bs) +
                                   static_cast<uint32_t>(row_in_page(a, t, pidx));
             const int64_t off = ok ? static_cast<int64_t>(slot) * tok_bytes + head_off : clamp_off;
-            k[u] = load_words<KW>(kc + off);
-            v[u] = load_words<KW>(vc + off);
+            k[u] = load_words_nt<KW>(kc + off);
+            v[u] = load_words_nt<KW>(vc + off);
         }
     }
 }
@@ -335,7 +335,8 @@ struct DecodeRun {
     int64_t tok_bytes;
     // the unit
     Unit un;
-    int n, n_dev, kb, ke, lo, h;  // lo: first key the row sees (its window)
+    int n, kb, ke, lo, h;  // lo: first key the row sees (its window)
+    bool stale;            // the device's lengths or row offsets differ from the plan's
     SeqTable tbl;
     uint32_t head_off, lane_off;
     int64_t clamp_off;
@@ -344,10 +345,6 @@ struct DecodeRun {
     float acc[G][EPL];
     float m_run, l_run;
     bool bad;
-    // page ids of the wave-tile at token pf_t of the open unit, loaded ahead
-    // (pf_t < 0: none)
-    int32_t pf_pages[kSubTiles<U>];
-    int pf_t;
 
     __device__ __forceinline__ explicit DecodeRun(const AttnArgs& a) {
         lane = threadIdx.x & 63;
@@ -365,13 +362,14 @@ struct DecodeRun {
 
     // The key range comes from the plan alone (a decode row sits at position
     // n - 1), so the first loads need not wait for a length read; the
-    // device length is read alongside and checked at the flush: a sequence
-    // whose length differs from the plan's (a stale plan) gets NaN rows.
+    // device length (and, in a packed batch, the row offsets) are read
+    // alongside and checked at the flush: a sequence whose length or rows
+    // differ from the plan's (a stale plan) gets NaN rows.
     __device__ __forceinline__ void open(const AttnArgs& a, const Unit& u, int head) {
         un = u;
         h = head;
         n = u.pos0 + 1;
-        n_dev = as_const(a.context_lens)[u.seq];
+        stale = unit_is_stale(a, u);
         kb = u.kv_begin;
         ke = min(u.kv_end, n);
         lo = a.window > 0 ? max(0, n - a.window) : 0;
@@ -391,15 +389,11 @@ struct DecodeRun {
         m_run = -INFINITY;  // running max of this lane's head (the head's lanes agree)
         l_run = 0.f;        // running sum of 2^(s - m_run) of this lane's head
         bad = false;
-        pf_t = -1;
     }
 
     // Keys [ta, tb) of the open unit (tb <= ke).  Tokens past tb are masked:
-    // they may belong to another workgroup's range.  `next` (a multiple of
-    // 16 past kv_begin, or -1) is where the caller expects its next range of
-    // this unit to start: the page ids of that wave-tile are loaded during
-    // the last tile of this range.
-    __device__ __forceinline__ void tiles(const AttnArgs& a, int ta, int tb, int next = -1) {
+    // they may belong to another workgroup's range.
+    __device__ __forceinline__ void tiles(const AttnArgs& a, int ta, int tb) {
         const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
         const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
         const int step = TT * tp;
@@ -408,15 +402,7 @@ struct DecodeRun {
         // wait for a table read.
         int32_t pages[kSubTiles<U>];
         int32_t lp[U];  // per-token pages: this lane's table entries
-        if constexpr (UNIFORM_PAGE) {
-            if (pf_t == ta + sub * TT) {
-#pragma unroll
-                for (int s = 0; s < kSubTiles<U>; ++s) pages[s] = pf_pages[s];
-            } else {
-                tile_pages<U>(pages, a, tbl, ta + sub * TT, tb);
-            }
-        }
-        pf_t = -1;
+        if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, ta + sub * TT, tb);
         const uint32_t vspan = static_cast<uint32_t>(max(tb - lo, 0));  // keys lo .. tb - 1 are valid
         // the loop is built twice, with and without the logit soft-cap, so
         // that the plain call's loop carries no test of it
@@ -432,12 +418,7 @@ struct DecodeRun {
                                                                head_off, tok_bytes, clamp_off, tbl.n, bad);
             }
             if constexpr (UNIFORM_PAGE) {
-                if (t0 + step < tb) {
-                    tile_pages<U>(pages, a, tbl, t0 + step, tb);
-                } else if (next >= kb && next < ke) {
-                    pf_t = next + sub * TT;
-                    tile_pages<U>(pf_pages, a, tbl, pf_t, ke);
-                }
+                if (t0 + step < tb) tile_pages<U>(pages, a, tbl, t0 + step, tb);
             }
             // lo <= t0 + my_tok < tb as one unsigned compare
             const bool valid = static_cast<uint32_t>(t0 - lo + my_tok) < vspan;
@@ -462,7 +443,7 @@ struct DecodeRun {
         });
 
         // merge the four rows of the wave
-        bool bd = __any(bad) || n_dev != n;
+        bool bd = __any(bad) || stale;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float M = rows4_max(m[g]);

@@ -1,10 +1,13 @@
 // Prefill chunks of a mixed step on the matrix cores (gfx950).
 //
-// A mixed step is two launches over one plan: the decode kernel walks the
-// decode queues (the decode rows run the decode unit unchanged, never a
-// gather) and this kernel walks the prefill queues.  ("nanoserve", packed
-// batches and chunked prefill: a mixed step goes to the decode kernel for its
-// one-row sequences and to a prefill kernel for its chunks.)
+// A mixed step walks one plan with two kinds of workgroup: decode workgroups
+// walk the decode queues (the decode rows run the decode unit unchanged,
+// never a gather) and prefill workgroups the prefill queues.  For bf16 K/V
+// on pages of whole 16-token tiles (groups 2 and 4) both run in one launch,
+// mixed_kernel, side by side on every compute unit; other cases launch the
+// decode kernel and prefill_kernel one after the other.  ("nanoserve", packed
+// batches and chunked prefill: a mixed step sends its one-row sequences to
+// the decode kernel and its chunks to a prefill path.)
 //
 // A prefill unit is a block of rows of one chunk, one kv head and one key
 // piece.  Its kPrefillQRows (row, q head) pairs are spread over the 8 waves,
@@ -333,9 +336,11 @@ struct PfWave {
         // every pair of the wave is a row of the unit
         wave_full = (wave * kPfPairsPerWave + kPfPairsPerWave - 1) / G < un.nrows;
 
-        const int n_ctx = as_const(a.context_lens)[un.seq];
         kb = un.kv_begin;
-        kend = min(min(un.kv_end, n_ctx), un.pos0 + un.nrows);  // no row sees past its position
+        kend = min(un.kv_end, un.pos0 + un.nrows);  // no row sees past its position
+        // a stale plan (lengths or row offsets of the sequence other than the
+        // plan's) makes every row of the unit NaN, as in the decode unit
+        bad = unit_is_stale(a, un);
         win = a.window > 0 ? a.window : INT32_MAX;
         tbl = seq_table(a, un.seq);
 
@@ -363,7 +368,6 @@ struct PfWave {
         for (int b = 0; b < ND; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         m_run = -INFINITY;  // running max of this lane's pair (its four lanes agree)
         l_run = 0.f;        // this lane's share of the running sum
-        bad = false;
     }
 
     // Tiles wholly past the wave's last row, or wholly before the first

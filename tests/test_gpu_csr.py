@@ -64,7 +64,7 @@ def test_csr_decode_full_size(gpu):
     check_close(got, ref, "bf16", f"csr decode merges={plan.desc.num_merges}")
 
 
-@pytest.mark.parametrize("bs,extra", [(16, 0), (16, 3), (1, 0), (3, 2), (32, 1)])
+@pytest.mark.parametrize("bs,extra", [(16, 0), (16, 3), (1, 0), (3, 2), (4, 0), (32, 1), (48, 1), (64, 2)])
 def test_csr_decode_page_sizes(gpu, bs, extra):
     log(f"csr decode bs={bs} extra={extra}")
     lens = [1, 17, 100, 250, 513, 64, 2000]
@@ -74,7 +74,7 @@ def test_csr_decode_page_sizes(gpu, bs, extra):
     check_close(got, ref, "bf16", f"csr bs={bs}")
 
 
-@pytest.mark.parametrize("bs", [16, 32, 3])
+@pytest.mark.parametrize("bs", [16, 32, 3, 4, 48, 64])
 def test_csr_mixed(gpu, bs):
     """Chunks and decodes through the CSR rows: page 16/32 run the
     direct-to-LDS prefill ring, page 3 the register-staged tiles."""

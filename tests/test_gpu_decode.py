@@ -44,7 +44,7 @@ def test_decode_workload_full_size(gpu):
     check_close(got, ref, "bf16", f"decode units={plan.desc.num_units} merges={plan.desc.num_merges}")
 
 
-@pytest.mark.parametrize("bs", [1, 3, 7, 16, 32])
+@pytest.mark.parametrize("bs", [1, 3, 4, 7, 16, 32, 48, 64])
 @pytest.mark.parametrize("num_queues", [1, 9, 0])
 def test_block_sizes(gpu, bs, num_queues):
     log(f"block size {bs} queues={num_queues}")

@@ -44,7 +44,7 @@ def test_mixed_workload_full_size(gpu):
     check_close(out[drow], ref[drow], "bf16", "mixed decode rows")
 
 
-@pytest.mark.parametrize("bs", [1, 3, 16, 32])
+@pytest.mark.parametrize("bs", [1, 3, 4, 16, 32, 48, 64])
 @pytest.mark.parametrize("num_queues", [1, 7, 0])
 def test_mixed_chunks_and_decodes(gpu, bs, num_queues):
     """Chunks of 2 .. 300 rows (ragged tails of the 32-row blocks and 32-key
@@ -167,3 +167,67 @@ def test_speculative_verify_rows(gpu, q_len):
                                 num_kv_heads=8, head_dim=128, block_size=16)
     out, ref, plan = _run(case, gpu)
     check_close(out, ref, "bf16", f"spec q_len={q_len} units={plan.desc.num_units} merges={plan.desc.num_merges}")
+
+
+@pytest.mark.parametrize("bs", [16, 3])
+def test_cu_seqlens_other_than_the_plan_gives_nan_rows(gpu, bs):
+    """cu_seqlens must be the prefix sums of the q_lens the plan was made
+    from.  Offsets that differ (here sequence 1 given two rows and sequence
+    2 none) turn the rows the plan gives those sequences into NaN, and leave
+    the chunk and the last decode row as the oracle has them; a shift of
+    every offset turns every row NaN.  Page 16 runs the one-launch mixed
+    kernel, page 3 the decode and prefill kernels one after the other."""
+    log(f"cu_seqlens mismatch bs={bs}")
+    lens, ql = [300, 50, 90, 70], [100, 1, 1, 1]
+    case = workloads.build_case("mxcu", 97, lens, ql, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=bs)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    plan = dc.plan(5, mixed=True)
+    good = as_f64(dc.mixed(plan))
+    check_close(good, ref, "bf16", "matching cu_seqlens")
+    assert list(case.cu_seqlens) == [0, 100, 101, 102, 103]
+    dc.cu = to_dev(np.array([0, 100, 102, 102, 103], np.int32), gpu)
+    out = as_f64(dc.mixed(plan))
+    assert np.all(np.isnan(out[100:102]))
+    check_close(out[np.r_[0:100, 102]], ref[np.r_[0:100, 102]], "bf16", "rows of the matching sequences")
+    dc.cu = to_dev(np.array([1, 101, 102, 103, 104], np.int32), gpu)
+    out = as_f64(dc.mixed(plan))
+    assert np.all(np.isnan(out))
+
+
+@pytest.mark.parametrize("bs", [16, 3])
+@pytest.mark.parametrize("change", [-1, 1])
+def test_stale_plan_length_gives_nan_chunk_rows(gpu, bs, change):
+    """A chunk's key ranges and positions come from the plan; a device length
+    other than the plan's (a stale plan) turns every row of the chunk into
+    NaN, as it does for decode rows, and leaves the other rows unaffected."""
+    log(f"stale chunk plan bs={bs} change={change}")
+    lens, ql = [700, 60, 1200], [130, 1, 1]
+    case = workloads.build_case("mxstale", 98, lens, ql, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                                block_size=bs)
+    dc = DeviceCase(case, gpu)
+    dc.write()
+    kr, vr = oracle_caches(case)
+    ref, _ = oracle_attention(case, kr, vr)
+    plan = dc.plan(6, mixed=True)
+    ctx = case.context_lens.copy()
+    ctx[0] += change
+    dc.ctx = to_dev(ctx, gpu)
+    out = as_f64(dc.mixed(plan))
+    assert np.all(np.isnan(out[:130]))
+    check_close(out[130:], ref[130:], "bf16", "rows of the unchanged sequences")
+
+
+@pytest.mark.parametrize("lens,ql", [([4000], [33]), ([4000, 3000], [33, 1]), ([4500, 900, 2500], [65, 1, 97])])
+def test_single_row_chunk_block_over_a_long_prefix(gpu, lens, ql):
+    """Chunks whose last row block holds one row (q_len = 1 mod 32 at 32/8
+    heads) over >= 4K keys, at the default queue count: that block is cut into
+    pieces and merged as a row block."""
+    log(f"single-row chunk block {lens} {ql}")
+    case = workloads.build_case("mx1row", 99, lens, ql, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                block_size=16)
+    out, ref, plan = _run(case, gpu)
+    assert plan.desc.num_block_merges >= 1
+    check_close(out, ref, "bf16", f"single-row block merges={plan.desc.num_merges}")

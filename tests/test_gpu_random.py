@@ -1,6 +1,6 @@
 """Seeded random batches through paged_attn_mixed against the fp64 oracle:
 random lengths (including whole-prompt chunks and single keys), query rows,
-page sizes (1, 3, 16, 32), head shapes, bf16 or fp8 caches, and the
+page sizes (1, 3, 4, 16, 32, 48, 64), head shapes, bf16 or fp8 caches, and the
 soft-cap / sliding-window variants, with a small queue count so that rows
 are cut and merged."""
 
@@ -23,7 +23,7 @@ def _draw(seed):
     whole = (rng.random(B) < 0.15) & (lens < 400)
     ql[whole] = lens[whole]
     hq, hkv, d = [(32, 8, 128), (16, 4, 64), (8, 8, 128), (16, 8, 64)][int(rng.integers(0, 4))]
-    bs = int(rng.choice([1, 3, 16, 32]))
+    bs = int(rng.choice([1, 3, 4, 16, 32, 48, 64]))
     kv = "fp8" if rng.random() < 0.25 else "bf16"
     cap = float(rng.choice([0.0, 0.0, 8.0]))
     window = int(rng.choice([0, 0, 33, 500]))

@@ -70,7 +70,7 @@ def test_window_decode(gpu, window):
     check_close(got, ref, "bf16", f"window {window}")
 
 
-@pytest.mark.parametrize("bs", [1, 3, 32])
+@pytest.mark.parametrize("bs", [1, 3, 4, 32, 48, 64])
 @pytest.mark.parametrize("hq,hkv,d", [(16, 4, 128), (8, 8, 64), (16, 2, 64)])
 def test_variants_decode_pages_and_groups(gpu, bs, hq, hkv, d):
     log(f"variants decode bs={bs} hq={hq} hkv={hkv} d={d}")
@@ -95,7 +95,7 @@ MIXED_LENS = [700, 1300, 2560, 130, 900, 45, 3000, 260]
 MIXED_Q = [1, 1, 512, 65, 1, 45, 4, 1]
 
 
-@pytest.mark.parametrize("bs", [16, 32, 3])
+@pytest.mark.parametrize("bs", [16, 32, 3, 48, 64])
 @pytest.mark.parametrize("soft_cap,window", [(0.0, 1), (0.0, 64), (0.0, 300), (0.0, 2000), (10.0, 0), (10.0, 129)])
 def test_variants_mixed(gpu, bs, soft_cap, window):
     """Chunks, a whole-prompt prefill (45 of 45), a speculative-verify row
