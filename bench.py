@@ -15,11 +15,13 @@ prefill chunk packed in one step; "nanoserve" chunked prefill) and
 ``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
 peak), ``specverify`` (64 sequences with 4 new rows each, a speculative
 verify step, through the mixed path).  ``--study skew``, ``--study
-plan-cost`` and ``--study pages`` print, instead of the bench line, one JSON
-line per case of the load-balance study (length mixes of equal total tokens
-at batch 4-128), the planner-cost sweep (batch 8-512) and the page-size
-sweep (pages of 1/4/16/64 tokens and a contiguous slab at 64 x 4K,
-16 x 16K and 256 x 1K keys).
+plan-cost``, ``--study pages`` and ``--study read-peak`` print, instead of
+the bench line, one JSON line per case of the load-balance study (length
+mixes of equal total tokens at batch 4-128), the planner-cost sweep (batch
+8-512), the page-size sweep (pages of 1/4/16/64 tokens and a contiguous slab
+at 64 x 4K, 16 x 16K and 256 x 1K keys, each case's layer 0 checked against
+the oracle on sampled sequences) and the measured read ceilings of the
+streaming-read probe.
 
 Inputs are synthetic: block tables, lengths and slots come from the seeded
 generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
@@ -230,6 +232,80 @@ def copy_calibration(torch):
           flush=True)
 
 
+PROBE_LIB = os.path.join(ROOT, "paged_kv_attention_write_amd", "libpkv_probe.so")
+
+
+def probe_read_GBps(torch, nbytes, reps=20, pages=None, page_bytes=0, pool=None):
+    """HBM read rate of the streaming probe (libpkv_probe.so): one persistent
+    8-wave workgroup per CU reading 16 bytes per lane, non-temporal.  Without
+    ``pages`` it reads ``nbytes`` contiguous bytes, rotating over four
+    disjoint windows of a buffer four times that size so that no launch finds
+    its bytes in the last-level cache; with ``pages`` (a device int32 list of
+    page ids into ``pool``, a uint8 device buffer of whole pages) it reads
+    those pages whole, in list order.  Median over ``reps`` launches timed
+    with HIP events on the current stream, in GB/s."""
+    import ctypes
+
+    L = ctypes.CDLL(PROBE_LIB)
+    L.pkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    L.pkv_probe_read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    blocks = int(props.multi_processor_count)
+    sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if pages is None:
+        nbytes = nbytes // 16 * 16
+        buf = torch.ones(4 * nbytes, dtype=torch.uint8, device=dev)
+        args = [(buf.data_ptr() + (i % 4) * nbytes, nbytes, None, 0, 0, 0) for i in range(reps + 4)]
+        moved = nbytes
+    else:
+        args = [(pool.data_ptr(), 0, pages.data_ptr(), pages.numel(), page_bytes, pool.numel() // page_bytes)] * (reps + 4)
+        moved = pages.numel() * page_bytes
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(args))]
+    for i, a in enumerate(args):
+        ev[2 * i].record(stream)
+        st = L.pkv_probe_read(*a, sink.data_ptr(), blocks, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"pkv_probe_read failed ({st})")
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(4, len(args))])
+    return moved / (float(np.median(ms)) * 1e-3) / 1e9
+
+
+def study_read_peak(args, torch, workloads):
+    """Measured read ceilings: the streaming probe over contiguous buffers of
+    the decode call's size and of 2 GiB, and over the K and V pages of the
+    decode workload's and the long workload's shuffled page-16 tables (each
+    page of 16 tokens x 8 kv heads x 128 x bf16 = 32 KiB read whole)."""
+    dev = torch.device("cuda:0")
+    from workloads import byte_model
+
+    st = workloads.structure_only("decode", "page16")
+    call = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, 16, 2, 2)
+    for nbytes in (call, 2 << 30):
+        gbs = probe_read_GBps(torch, nbytes)
+        print(json.dumps({"study": "read-peak", "pattern": "contiguous", "bytes": int(nbytes // 16 * 16),
+                          "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / 8000.0, 4)}), flush=True)
+    page_bytes = 16 * 8 * 128 * 2
+    for config, layout in (("decode", "page16"), ("long", "page16")):
+        st = workloads.structure_only(config, layout)
+        nb = int(st["num_blocks"])
+        used = np.concatenate([st["block_tables"][s, :-(-int(n) // 16)]
+                               for s, n in enumerate(st["context_lens"])]).astype(np.int64)
+        ids = np.stack([used, used + nb], axis=1).reshape(-1).astype(np.int32)  # K page, then its V page
+        pool = torch.ones(2 * nb * page_bytes, dtype=torch.uint8, device=dev)
+        pages = torch.from_numpy(ids).to(dev)
+        gbs = probe_read_GBps(torch, 0, pages=pages, page_bytes=page_bytes, pool=pool)
+        print(json.dumps({"study": "read-peak", "pattern": f"{config} K/V pages (page 16, shuffled)",
+                          "pages": int(ids.size), "bytes": int(ids.size * page_bytes), "GBps": round(gbs, 1),
+                          "frac_of_8TBps": round(gbs / 8000.0, 4)}), flush=True)
+        del pool, pages
+        torch.cuda.empty_cache()
+
+
 def queue_balance(pkv, st, num_queues):
     """Largest over mean decode-queue load of the host plan, in 16-key tiles."""
     from paged_kv_attention_write_amd import _abi
@@ -328,15 +404,46 @@ def study_pages(args, torch, pkv, workloads, byte_model):
             p50 = float(np.median(ms)) * 1e-3
             if layout == "contiguous":
                 ref_us = p50
+            cb = pages_cpu_baseline(torch, st, layers[0], scale)
             print(json.dumps({
                 "study": "pages", "batch": batch, "context": n, "layout": layout, "block_size": bs,
                 "table_entries": int(st["block_tables"].size),
                 "call_us": {"p10": round(float(np.percentile(ms, 10)) * 1e3, 2), "p50": round(p50 * 1e6, 2),
                             "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
                 "TBps": round(nbytes / p50 / 1e12, 4), "frac_of_8TBps": round(nbytes / p50 / 8e12, 4),
-                "vs_contiguous": round(ref_us / p50, 4), "layers": len(layers)}), flush=True)
+                "vs_contiguous": round(ref_us / p50, 4), "layers": len(layers), "cpu_baseline": cb}), flush=True)
+            if not cb["parity"]["ok"]:
+                raise SystemExit(f"page-size sweep: layer 0 differs from the oracle at {layout} page {bs}")
             del layers, plan, tables
             torch.cuda.empty_cache()
+
+
+def pages_cpu_baseline(torch, st, layer, scale, samples=6):
+    """The cpu_baseline leg of a page-size sweep case: the fp64 oracle timed
+    on a sample of sequences of layer 0 (first, last and evenly spaced ones),
+    and layer 0's output of the timed calls compared with it under the
+    library's bf16 bound (max-abs 2e-2 and 2^-7 of the largest |output|)."""
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    B = st["context_lens"].shape[0]
+    seqs = sorted(set(np.linspace(0, B - 1, samples).round().astype(int).tolist()))
+    kc, vc, q = host(layer["kc"]), host(layer["vc"]), host(layer["q"])
+    t0 = time.perf_counter()
+    ref, _ = oracle.paged_attention(q, "bf16", kc, vc, "bf16", st["block_tables"], st["context_lens"],
+                                    st["cu_seqlens"], scale, seqs=seqs)
+    el = time.perf_counter() - t0
+    got = layer["out"].float().cpu().numpy().astype(np.float64)
+    rows = np.asarray(seqs)
+    err = float(np.max(np.abs(got[rows] - ref[rows])))
+    bound = min(2e-2, 1e-4 + 2.0 ** -7 * float(np.max(np.abs(ref[rows]))))
+    toks = int(st["context_lens"][rows].sum())
+    return {"kind": "oracle", "sample": f"sequences {seqs} of layer 0", "seconds": round(el, 3),
+            "TBps": toks * 4096 / el / 1e12, "cores": len(os.sched_getaffinity(0)),
+            "parity": {"max_abs_err": err, "bound": bound, "ok": bool(np.all(np.isfinite(got[rows])) and err <= bound)}}
 
 
 def study_plan_cost(args, torch, pkv, workloads):
@@ -368,7 +475,7 @@ def main():
     ap.add_argument("--config", default="decode", choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--queues", type=int, default=0, help="planner queues (0: the library default, 2 per CU)")
+    ap.add_argument("--queues", type=int, default=0, help="planner decode queues (0: the library default, one per CU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
@@ -379,9 +486,11 @@ def main():
                     help="attention variant: logit soft-cap c (scores through c * tanh(s / c)); 0: off")
     ap.add_argument("--window", type=int, default=0,
                     help="attention variant: sliding window of W keys (a row at p sees p - W < j <= p); 0: off")
-    ap.add_argument("--study", choices=["skew", "plan-cost", "pages"],
-                    help="instead of the bench line: the load-balance study over length mixes (skew) or the "
-                         "planner cost over batch sizes (plan-cost), one JSON line per case")
+    ap.add_argument("--study", choices=["skew", "plan-cost", "pages", "read-peak"],
+                    help="instead of the bench line: the load-balance study over length mixes (skew), the "
+                         "planner cost over batch sizes (plan-cost), the page-size sweep with its parity check "
+                         "(pages) or the streaming-read ceilings of the read probe (read-peak), one JSON line "
+                         "per case")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); sharding across GPUs is not built",
@@ -406,6 +515,9 @@ def main():
         return
     if args.study == "pages":
         study_pages(args, torch, pkv, workloads, byte_model)
+        return
+    if args.study == "read-peak":
+        study_read_peak(args, torch, workloads)
         return
 
     cfg = CONFIGS[args.config]
@@ -558,6 +670,13 @@ def main():
     if mixed:
         roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                              "chunk_tflops": round(mfma_tflops, 2)}
+    # the device's measured streaming-read rate for as many bytes as one call
+    # reads, beside the published peak
+    peak_gbs = probe_read_GBps(torch, attn_bytes)
+    roofline["measured_peak"] = {"value": round(peak_gbs, 1), "unit": "GB/s",
+                                 "what": "streaming-read probe (libpkv_probe.so): contiguous, 16 B per lane, "
+                                         "non-temporal, one 8-wave workgroup per CU, as many bytes as one call"}
+    roofline["frac_of_measured_peak"] = round(attn_bytes / call_s / 1e9 / peak_gbs, 4)
 
     variant_desc = "".join([f", soft-cap {args.soft_cap:g}" if args.soft_cap else "",
                             f", window {args.window}" if args.window else ""])

@@ -1,8 +1,10 @@
-"""Build the HIP library ``libpkv.so`` for gfx950, in-tree.
+"""Build the HIP libraries for gfx950, in-tree.
 
-Every source under ``csrc/`` is compiled with hipcc for gfx950 only, with
-packed-fp32 instructions disabled, and linked into one shared library next to
-this file.  ``python -m paged_kv_attention_write_amd.build`` runs it.
+The attention library ``libpkv.so`` is linked from every source under
+``csrc/`` but the read-bandwidth probe, which the benchmark loads on its own
+as ``libpkv_probe.so``.  Everything is compiled with hipcc for gfx950 only,
+with packed-fp32 instructions disabled.  ``python -m
+paged_kv_attention_write_amd.build`` runs it.
 """
 
 from __future__ import annotations
@@ -18,9 +20,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["pkv_plan.cpp", "pkv_api.cpp", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip"]
+PROBE_SOURCES = ["pkv_probe.hip"]
 
 COMMON = [
     "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
@@ -47,18 +51,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
