@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 /* Status codes. */
 #define PKV_OK 0
@@ -346,6 +346,36 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
                      int32_t head_dim, int64_t num_blocks, int32_t block_size, float scale, float k_scale,
                      float v_scale, const pkv_plan* plan, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * paged_attn_decode_noalloc - paged_attn_decode for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, serving loops
+ * that must not allocate, harnesses that forbid it): the workspace is the
+ * library's own device array of 32 MiB (one per device, held until the
+ * process ends) instead of a caller buffer, and the call allocates nothing.
+ *
+ *   plan, plan_image_host   a decode plan (q_lens NULL or all ones) and its
+ *                           image, from paged_attn_plan_host or the host-only
+ *                           form of paged_attn_plan_variant; the call copies
+ *                           the image into the array on `stream` (pinned
+ *                           host memory makes the copy asynchronous; it must
+ *                           stay unchanged until the copy has run)
+ * Every other argument as for paged_attn_decode.  Nothing in the array needs
+ * to start at zero: the copy writes the plan, and every partial result is
+ * written before the merge reads it.
+ * Errors as paged_attn_decode, plus PKV_ERR_WORKSPACE when the plan needs
+ * more than the 32 MiB array (plan->workspace_bytes; checked before any
+ * device work) and PKV_ERR_NULL for a NULL image with rows to compute.
+ * Calls on one device share its array: calls that overlap in time on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller, like calls that share a workspace.
+ */
+int paged_attn_decode_noalloc(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride,
+                              const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                              const pkv_plan* plan, const void* plan_image_host, void* stream);
 
 /*
  * paged_attn_decode_csr / paged_attn_mixed_csr - paged_attn_decode and

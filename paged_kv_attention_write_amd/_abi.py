@@ -49,6 +49,7 @@ EXPORTS = (
     "paged_attn_mixed",
     "paged_attn_decode_csr",
     "paged_attn_mixed_csr",
+    "paged_attn_decode_noalloc",
 )
 
 
@@ -135,6 +136,10 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_mixed_csr.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                            i64, i32, f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_mixed_csr.restype = ctypes.c_int
+        # the entry point that allocates nothing: the plan image (host) in place of the workspace
+        L.paged_attn_decode_noalloc.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i64,
+                                                i32, f32, f32, f32, P(PkvPlan), vp, vp]
+        L.paged_attn_decode_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 

@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
 ARCH = "gfx950"
 
-SOURCES = ["pkv_plan.cpp", "pkv_api.cpp", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip"]
+SOURCES = ["pkv_plan.cpp", "pkv_api.cpp", "pkv_write.hip", "pkv_decode.hip", "pkv_prefill.hip", "pkv_noalloc.hip"]
 PROBE_SOURCES = ["pkv_probe.hip"]
 
 COMMON = [

@@ -286,6 +286,38 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
                        scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
 }
 
+int paged_attn_decode_noalloc(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride,
+                              const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                              const pkv_plan* plan, const void* plan_image_host, void* stream) {
+    if (plan == nullptr) return PKV_ERR_NULL;
+    // the plan must fit the scratch array; checked before any HIP call
+    if (plan->magic != PKV_PLAN_MAGIC) return PKV_ERR_PLAN;
+    if (plan->workspace_bytes < 0 || static_cast<size_t>(plan->workspace_bytes) > kNoallocScratchBytes)
+        return PKV_ERR_WORKSPACE;
+    if (block_tables == nullptr && num_seqs > 0) return PKV_ERR_NULL;
+    if (num_seqs > 0 && plan->image_bytes > 0 && plan_image_host == nullptr) return PKV_ERR_NULL;
+    // every check of the attention call before any HIP call; the scratch
+    // array stands in as the workspace (non-null, aligned, of its size)
+    int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                             max_blocks_per_seq, context_lens, num_seqs, num_seqs, num_q_heads, num_kv_heads,
+                             head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan,
+                             reinterpret_cast<void*>(kAlign), kNoallocScratchBytes);
+    if (st != PKV_OK || num_seqs == 0) return st;
+    if (plan->max_q_len > 1) return PKV_ERR_PLAN;
+    void* ws = nullptr;
+    st = noalloc_scratch(&ws);
+    if (st != PKV_OK) return st;
+    if (hipMemcpyAsync(ws, plan_image_host, static_cast<size_t>(plan->image_bytes), hipMemcpyHostToDevice,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+        return PKV_ERR_HIP;
+    return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                       nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       scale, k_scale, v_scale, plan, ws, kNoallocScratchBytes, stream);
+}
+
 int paged_attn_decode_csr(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
                           const void* v_cache, int32_t kv_dtype, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* context_lens, int32_t num_seqs,

@@ -92,6 +92,12 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
               size_t host_bytes, pkv_plan* plan, int32_t cap_seqs = -1, int32_t cap_tokens = -1,
               float soft_cap = 0.f, int32_t window = 0);
 
+// Size of the device scratch array of the entry point that allocates nothing
+// (one per device, held until the process ends), and its device address on
+// the current device (pkv_noalloc.hip; asked of the runtime once per device).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+int noalloc_scratch(void** ptr);
+
 // Upper bounds used by paged_attn_workspace_size.
 void plan_bounds(int32_t max_seqs, int32_t max_tokens, int32_t num_q_heads, int32_t head_dim,
                  int32_t num_queues, size_t* workspace_bytes, size_t* host_bytes);

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.pkv_abi_version() == 4
+    assert L.pkv_abi_version() == 5
 
 
 def test_strerror_covers_all_codes():
