@@ -38,6 +38,12 @@ struct DecodeRegs {
     // bf16 q against bf16 or fp8 keys: q . k in bf16 pairs (an fp8 key is
     // exactly a bf16 value)
     static constexpr bool kDot2 = QDT == PKV_DTYPE_BF16 && (KVDT == PKV_DTYPE_BF16 || KVDT == PKV_DTYPE_FP8_E4M3);
+    // P V as bf16 pairs over two tokens (one v_dot2_f32_bf16 per element,
+    // head and token pair), the weights rounded to bf16 and the softmax sum
+    // taken over the rounded weights (as the prefill tile rounds P for its
+    // matrix product): half the vector instructions of fp32 weights times
+    // widened values
+    static constexpr bool kPvDot2 = kDot2;
 };
 
 // Query slice of one head held by a lane: bf16 pairs (dot2 path) or fp32.
@@ -100,9 +106,32 @@ __device__ __forceinline__ uint32_t key_pair(const Words<KW>& r, int j) {
     if constexpr (KVDT == PKV_DTYPE_BF16) {
         return r.w[j];
     } else {
+        // two E4M3 codes to two bf16 values in one instruction (scale 1)
         const int w = static_cast<int>(r.w[j >> 1]);
-        const float2_t f = (j & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-        return (__float_as_uint(f.y) & 0xffff0000u) | (__float_as_uint(f.x) >> 16);
+        const bf16x2_t b = (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                   : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+        return __builtin_bit_cast(uint32_t, b);
+    }
+}
+
+// Element e of two tokens' slices as one bf16 pair (token a low, token b
+// high), for e = 2k (lo) and e = 2k + 1 (hi): the V operand of a P V product
+// over a token pair.
+template <int KVDT, int KW, int NP>
+__device__ __forceinline__ void token_pairs(uint32_t (&lo)[NP], uint32_t (&hi)[NP], const Words<KW>& a,
+                                            const Words<KW>& b) {
+    // slices as NP bf16 pairs of one token: elements (2k, 2k + 1)
+    static_assert(NP == (KVDT == PKV_DTYPE_BF16 ? KW : 2 * KW), "bf16 pairs of a slice");
+    uint32_t pa[NP], pb[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        pa[k] = key_pair<KVDT, KW>(a, k);
+        pb[k] = key_pair<KVDT, KW>(b, k);
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        lo[k] = __builtin_amdgcn_perm(pb[k], pa[k], 0x05040100u);  // (a[2k], b[2k])
+        hi[k] = __builtin_amdgcn_perm(pb[k], pa[k], 0x07060302u);  // (a[2k + 1], b[2k + 1])
     }
 }
 
@@ -289,16 +318,45 @@ __device__ __forceinline__ void process_tile(const Words<KW> (&k)[U], const Word
         });
     }
     const float p = exp2_fast(sc - ((m_run == -INFINITY) ? 0.f : m_run));
-    l_run += row_group_sum<G>(p);
-    static_for<U>([&](auto u) {
-        float vf[EPL];
-        kv_to_f32<KVDT, EPL, KW>(vf, v[u]);
-        static_for<G>([&](auto g) {
-            const float pb = row_bcast<u * G + g>(p);
+    if constexpr (R::kPvDot2) {
+        // lane col c holds the weight of token 4 (c / G) + row and head c % G;
+        // lane c + G holds the same head's weight of the next token.  Each
+        // lane packs the two as bf16 (round to nearest even); the pair of
+        // tokens 2j, 2j + 1 and head g sits in lane 2 j G + g.  The row sum
+        // adds the rounded weights, so the output is a convex combination of
+        // V rows under the weights P V uses.
+        const float pn = dpp_f32<kDppRowRor + (16 - G)>(p);  // lane c + G (mod 16)
+        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){p, pn}, bf16x2_t));
+        l_run += row_group_sum<G>(__uint_as_float(pk << 16));
+        static_for<U / 2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            uint32_t vlo[EPL / 2], vhi[EPL / 2];
+            token_pairs<KVDT, KW, EPL / 2>(vlo, vhi, v[2 * j], v[2 * j + 1]);
+            static_for<G>([&](auto g) {
+                const bf16x2_t pb = __builtin_bit_cast(
+                    bf16x2_t, __builtin_amdgcn_mov_dpp(static_cast<int>(pk), kDppRowNewBcast + 2 * j * G + g, 0xF,
+                                                       0xF, true));
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pb, vf[e], acc[g][e]);
+                for (int k = 0; k < EPL / 2; ++k) {
+                    acc[g][2 * k] = __builtin_amdgcn_fdot2_f32_bf16(pb, __builtin_bit_cast(bf16x2_t, vlo[k]),
+                                                                   acc[g][2 * k], false);
+                    acc[g][2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(pb, __builtin_bit_cast(bf16x2_t, vhi[k]),
+                                                                       acc[g][2 * k + 1], false);
+                }
+            });
         });
-    });
+    } else {
+        l_run += row_group_sum<G>(p);
+        static_for<U>([&](auto u) {
+            float vf[EPL];
+            kv_to_f32<KVDT, EPL, KW>(vf, v[u]);
+            static_for<G>([&](auto g) {
+                const float pb = row_bcast<u * G + g>(p);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pb, vf[e], acc[g][e]);
+            });
+        });
+    }
 }
 
 // LDS of the decode unit: the per-wave results that are merged across the

@@ -24,7 +24,7 @@ constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15 - i
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i within each half row (i ^ 7)
 constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppRowRor = 0x120;         // + n: lane i <- lane (i + n) mod 16
+constexpr int kDppRowRor = 0x120;         // + n (rotate right): lane i <- lane (i - n) mod 16
 constexpr int kDppRowNewBcast = 0x150;    // + n: every lane of the row <- lane n of the row
 
 template <int CTRL>
