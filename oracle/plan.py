@@ -26,6 +26,11 @@ Readings of what the illustration leaves open:
   workload at 256 queues: the largest queue holds 1.61x the mean work with
   the illustration's steps and 1.02x with this reading.
 * Requests with no keys get no piece.
+* ``unit_cost`` (tiles): every piece also adds this much to its queue's load
+  (the set-up of a unit of work: its first table reads and loads, its
+  flush), and the target grows by that much per queue.  0 is the page's
+  reading; the library plans with 1, the set-up time of a unit it measured
+  as about one tile's.
 
 ``split_kv_plan`` returns a list of queues; each queue is a list of
 ``(request, kv_begin, kv_end)`` token ranges in the order they were placed.
@@ -42,7 +47,7 @@ def split_lengths(kv_lens, tile: int = TILE_TOKENS):
     return [-(-int(n) // tile) for n in kv_lens]
 
 
-def split_kv_plan(kv_lens, num_queues: int, tile: int = TILE_TOKENS):
+def split_kv_plan(kv_lens, num_queues: int, tile: int = TILE_TOKENS, unit_cost: int = 0):
     """Return ``queues``: ``num_queues`` lists of ``(request, kv_begin, kv_end)``."""
     if num_queues < 1:
         raise ValueError("num_queues must be >= 1")
@@ -52,7 +57,7 @@ def split_kv_plan(kv_lens, num_queues: int, tile: int = TILE_TOKENS):
     queues = [[] for _ in range(num_queues)]
     if total == 0:
         return queues
-    target = -(-total // num_queues)
+    target = -(-(total + unit_cost * num_queues) // num_queues)
     loads = [0] * num_queues
     order = sorted(range(len(lens)), key=lambda r: (-lens[r], r))
     for r in order:
@@ -60,11 +65,12 @@ def split_kv_plan(kv_lens, num_queues: int, tile: int = TILE_TOKENS):
         first_tile = 0
         while remaining > 0:
             lightest = min(range(num_queues), key=lambda q: (loads[q], q))
-            take = min(remaining, target - loads[lightest])
+            room = target - loads[lightest] - unit_cost
+            take = min(remaining, room) if room > 0 else remaining
             begin = first_tile * tile
             end = min(lens[r], (first_tile + take) * tile)
             queues[lightest].append((r, begin, end))
-            loads[lightest] += take
+            loads[lightest] += take + unit_cost
             remaining -= take
             first_tile += take
     return queues

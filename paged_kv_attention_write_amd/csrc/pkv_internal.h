@@ -25,6 +25,12 @@ constexpr int kPrefillPieceMin = 512;
 // workgroups per CU when the decode launch runs one.
 constexpr int kPrefillQueuesPerQueue = 2;
 
+// Decode queue loads count each piece placed on a queue as this many tiles
+// more than its keys: the set-up of a unit (its first page lookups and
+// loads, its flush) costs about one tile's time, so a queue that runs two
+// pieces is given about a tile less.
+constexpr int kDecodeUnitCost = 1;
+
 // Alignment of the sections of the workspace.
 // A one-row merge record with at least this many pieces is "wide": its
 // merge gives every q head a workgroup whose waves split the pieces.

@@ -8,6 +8,9 @@
 // cut to what the least-loaded queue can still take before it reaches the
 // share, so queues end within one tile of each other and a request is cut
 // only where a queue fills up (at most queues + requests pieces in all).
+// Every piece also counts one tile of set-up in its queue's load (and the
+// share includes one per queue), so a queue running two pieces gets about
+// one tile less.
 //
 // Query chunks (more than one new row) are split into blocks of rows, one
 // unit per (row block, kv head, key piece), and run as a launch of their own
@@ -210,8 +213,10 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         }
     }
 
-    // The decode share: the decode tiles over the queues.
-    const int64_t target = decode_tiles > 0 ? ceil_div(decode_tiles, num_queues) : 0;
+    // The decode share: the decode tiles and a unit's set-up per queue, over
+    // the queues.
+    const int64_t target =
+        decode_tiles > 0 ? ceil_div(decode_tiles + static_cast<int64_t>(kDecodeUnitCost) * num_queues, num_queues) : 0;
     std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
     QueueHeap heap(num_queues);
 
@@ -232,14 +237,16 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         placed.clear();
         while (remaining > 0) {
             auto [load, q] = heap.pop();
-            // never reached while a queue is below the share; kept so that a
-            // full lightest queue takes the rest instead of looping
-            const int64_t take = target > load ? std::min(remaining, target - load) : remaining;
+            // what the lightest queue can still take after a unit's set-up;
+            // a full lightest queue (never reached while a queue is below the
+            // share) takes the rest instead of looping
+            const int64_t room = target - load - kDecodeUnitCost;
+            const int64_t take = room > 0 ? std::min(remaining, room) : remaining;
             const int32_t kb = static_cast<int32_t>(start + first * kTileTokens);
             const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, start + (first + take) * kTileTokens));
             queues[q].push_back(Unit{s, kb, ke, row0[s], 1, n - 1, -1, kUnitDecode});
             placed.emplace_back(q, queues[q].size() - 1);
-            heap.push(load + take, q);
+            heap.push(load + take + kDecodeUnitCost, q);
             remaining -= take;
             first += take;
         }

@@ -58,7 +58,7 @@ def test_native_plan_equals_oracle_plan(seed, nq):
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, 5000, size=int(rng.integers(1, 100)))
     p, image = pkv.plan_host(lens, None, 32, 8, 128, nq)
-    assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq)
+    assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq, unit_cost=1)
 
 
 @pytest.mark.parametrize("config", ["tiny", "decode", "long", "fp8prefix"])
@@ -68,7 +68,7 @@ def test_native_plan_equals_oracle_plan_on_workloads(config):
     lens = workloads.decode_lengths(config)
     for nq in (256, 512):
         p, image = pkv.plan_host(lens, None, 32, 8, 128, nq)
-        assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq)
+        assert _queues_from_image(p, image) == split_kv_plan(lens.tolist(), nq, unit_cost=1)
 
 
 def test_plan_partials_and_merges_are_consistent():
@@ -220,13 +220,14 @@ def test_variant_plan_rejects_bad_variants():
 
 def test_window_shrinks_decode_work():
     """Long decode rows under a window read only the last W keys (rounded
-    down to a tile): the share per queue follows the windowed work."""
+    down to a tile): the share per queue follows the windowed work (plus one
+    tile of set-up per queue)."""
     lens = np.full(64, 8192, np.int32)
     p, image = pkv.plan_host(lens, None, 32, 8, 128, 256, window=1000)
     units, _, _ = pkv.decode_plan_image(p, image)
     keys = int((units[:, 2] - units[:, 1]).sum())
     assert keys == 64 * (8192 - (8192 - 1000) // 16 * 16)
-    assert p.target_tiles == -(-keys // 16 // 256)
+    assert p.target_tiles == -(-(keys // 16 + 256) // 256)
 
 
 def test_mixed_plan_decode_queues_equal_the_decode_plan():
@@ -239,7 +240,7 @@ def test_mixed_plan_decode_queues_equal_the_decode_plan():
     npq = p.num_prefill_queues
     assert npq == 2 * nq and len(qoff) == nq + npq + 1
     dec = np.nonzero(ql == 1)[0]
-    want = split_kv_plan(lens[dec].tolist(), nq)
+    want = split_kv_plan(lens[dec].tolist(), nq, unit_cost=1)
     got = [[(int(dec.tolist().index(u[0])), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]]
            for q in range(nq)]
     assert got == want
