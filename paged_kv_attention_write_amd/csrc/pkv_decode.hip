@@ -287,6 +287,9 @@ int launch_decode_t(const AttnArgs& a, int num_queues, bool uniform, hipStream_t
                                    a);
         } else if (uniform) {
             hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, 2>), grid, dim3(8 * 64), 0, st, a);
+        } else if constexpr (G == 2 && D == 128) {
+            // eight tokens per lane and wave-tile need more than 128 registers
+            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, false, 2>), grid, dim3(8 * 64), 0, st, a);
         } else {
             hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, false, 4>), grid, dim3(16 * 64), 0, st, a);
         }
