@@ -8,7 +8,7 @@
 namespace pkv {
 namespace {
 
-template <int QDT, int KVDT, int D, int G, int NW, bool UNIFORM_PAGE, int WPE>
+template <int QDT, int KVDT, int D, int G, int NW, int PK, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void decode_kernel(AttnArgs a) {
     __shared__ DecodeLds<D, G, NW> lds;
@@ -18,7 +18,7 @@ void decode_kernel(AttnArgs a) {
     const int u_end = qoff[blockIdx.x + 1];
     for (int ui = u_begin; ui < u_end; ++ui) {
         const Unit un = load_unit(units, ui);
-        decode_unit<QDT, KVDT, D, G, NW, UNIFORM_PAGE>(a, un, lds);
+        decode_unit<QDT, KVDT, D, G, NW, PK>(a, un, lds);
     }
 }
 
@@ -268,55 +268,69 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const Merge* __
 // pattern).  One 8-wave workgroup per CU is two waves per SIMD, so those
 // kernels are built for two (up to 256 VGPRs): the register room lets the
 // compiler schedule the loads of a tile earlier than a 128-VGPR build does,
-// which measured 2.4 % faster on the 64-sequence decode batch.  16 waves (two per kv head, alternate tiles, <= 128 VGPRs) hide
-// the extra latency of per-token page lookups and the fp8 conversion work.
-// Group 8 (eight q heads per lane), group 1 (sixteen tokens in flight per
-// lane) and fp32 K/V need more registers and keep 8 waves at two waves per
+// which measured 2.4 % faster on the 64-sequence decode batch.  16 waves
+// (two per kv head, alternate tiles, <= 128 VGPRs) hide the extra latency
+// of per-lane page lookups (page sizes other than 1, 4, 8 and multiples of
+// 16) and the fp8 conversion work.  Group 8 (eight q heads per lane), group
+// 1 (sixteen tokens in flight per lane), group 2 on per-lane pages at
+// D = 128 and fp32 K/V need more registers and keep 8 waves at two waves per
 // SIMD.
+template <int QDT, int KVDT, int D, int G, int NW, int PK, int WPE>
+void launch_decode_kernel(const AttnArgs& a, int num_queues, hipStream_t st) {
+    hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, NW, PK, WPE>), dim3(num_queues), dim3(NW * 64), 0, st, a);
+}
+
+// A decode kernel shape for every page kind it serves: whole tiles, groups
+// of 4 or 8 tokens, one-token pages (ONE: groups 2 to 8 with the register
+// room for a wave-tile's next entries; otherwise they take the kPageAny
+// kernel) and any other size.
+template <int QDT, int KVDT, int D, int G, int NW, int WPE, bool ONE>
+void launch_decode_pk(const AttnArgs& a, int num_queues, int pk, hipStream_t st) {
+    if (pk == kPageTile)
+        launch_decode_kernel<QDT, KVDT, D, G, NW, kPageTile, WPE>(a, num_queues, st);
+    else if (pk == kPageGroup)
+        launch_decode_kernel<QDT, KVDT, D, G, NW, kPageGroup, WPE>(a, num_queues, st);
+    else if (ONE && pk == kPageOne)
+        launch_decode_kernel<QDT, KVDT, D, G, NW, (ONE ? kPageOne : kPageAny), WPE>(a, num_queues, st);
+    else
+        launch_decode_kernel<QDT, KVDT, D, G, NW, kPageAny, WPE>(a, num_queues, st);
+}
+
 template <int QDT, int KVDT, int D, int G>
-int launch_decode_t(const AttnArgs& a, int num_queues, bool uniform, hipStream_t st) {
+int launch_decode_t(const AttnArgs& a, int num_queues, int pk, hipStream_t st) {
     constexpr bool kSmallRegs = !(G == 8 || G == 1 || KVDT == PKV_DTYPE_F32);
-    const dim3 grid(num_queues);
     if constexpr (kSmallRegs) {
         if constexpr (KVDT == PKV_DTYPE_FP8_E4M3) {
-            if (uniform)
-                hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, true, 4>), grid, dim3(16 * 64), 0, st,
-                                   a);
-            else
-                hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, false, 4>), grid, dim3(16 * 64), 0, st,
-                                   a);
-        } else if (uniform) {
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, 2>), grid, dim3(8 * 64), 0, st, a);
+            launch_decode_pk<QDT, KVDT, D, G, 16, 4, false>(a, num_queues, pk, st);
+        } else if (pk != kPageAny) {
+            launch_decode_pk<QDT, KVDT, D, G, 8, 2, true>(a, num_queues, pk, st);
         } else if constexpr (G == 2 && D == 128) {
             // eight tokens per lane and wave-tile need more than 128 registers
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, false, 2>), grid, dim3(8 * 64), 0, st, a);
+            launch_decode_kernel<QDT, KVDT, D, G, 8, kPageAny, 2>(a, num_queues, st);
         } else {
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 16, false, 4>), grid, dim3(16 * 64), 0, st, a);
+            launch_decode_kernel<QDT, KVDT, D, G, 16, kPageAny, 4>(a, num_queues, st);
         }
     } else {
-        if (uniform)
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, true, 2>), grid, dim3(8 * 64), 0, st, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<QDT, KVDT, D, G, 8, false, 2>), grid, dim3(8 * 64), 0, st, a);
+        launch_decode_pk<QDT, KVDT, D, G, 8, 2, (G >= 2 && KVDT != PKV_DTYPE_F32)>(a, num_queues, pk, st);
     }
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 template <int QDT, int KVDT, int D>
-int launch_decode_g(const AttnArgs& a, int group, int num_queues, bool uniform, hipStream_t st) {
+int launch_decode_g(const AttnArgs& a, int group, int num_queues, int pk, hipStream_t st) {
     switch (group) {
-        case 1: return launch_decode_t<QDT, KVDT, D, 1>(a, num_queues, uniform, st);
-        case 2: return launch_decode_t<QDT, KVDT, D, 2>(a, num_queues, uniform, st);
-        case 4: return launch_decode_t<QDT, KVDT, D, 4>(a, num_queues, uniform, st);
-        case 8: return launch_decode_t<QDT, KVDT, D, 8>(a, num_queues, uniform, st);
+        case 1: return launch_decode_t<QDT, KVDT, D, 1>(a, num_queues, pk, st);
+        case 2: return launch_decode_t<QDT, KVDT, D, 2>(a, num_queues, pk, st);
+        case 4: return launch_decode_t<QDT, KVDT, D, 4>(a, num_queues, pk, st);
+        case 8: return launch_decode_t<QDT, KVDT, D, 8>(a, num_queues, pk, st);
         default: return PKV_ERR_UNSUPPORTED;
     }
 }
 
 template <int QDT, int KVDT>
-int launch_decode_d(const AttnArgs& a, int d, int group, int num_queues, bool uniform, hipStream_t st) {
-    if (d == 64) return launch_decode_g<QDT, KVDT, 64>(a, group, num_queues, uniform, st);
-    if (d == 128) return launch_decode_g<QDT, KVDT, 128>(a, group, num_queues, uniform, st);
+int launch_decode_d(const AttnArgs& a, int d, int group, int num_queues, int pk, hipStream_t st) {
+    if (d == 64) return launch_decode_g<QDT, KVDT, 64>(a, group, num_queues, pk, st);
+    if (d == 128) return launch_decode_g<QDT, KVDT, 128>(a, group, num_queues, pk, st);
     return PKV_ERR_UNSUPPORTED;
 }
 
@@ -325,13 +339,19 @@ int launch_decode_d(const AttnArgs& a, int d, int group, int num_queues, bool un
 int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool uniform = (a.block_size % kTileTokens) == 0;
+    // the page kind: whole 16-token tiles, groups of 4 tokens, one token,
+    // anything else
+    const int bs = a.block_size;
+    const int pk = bs % kTileTokens == 0 ? kPageTile
+                   : (bs == 4 || bs == 8) ? kPageGroup
+                   : (bs == 1 && group >= 2) ? kPageOne
+                                             : kPageAny;
     if (q_dtype == PKV_DTYPE_F32 && kv_dtype == PKV_DTYPE_F32)
-        return launch_decode_d<PKV_DTYPE_F32, PKV_DTYPE_F32>(a, head_dim, group, num_queues, uniform, st);
+        return launch_decode_d<PKV_DTYPE_F32, PKV_DTYPE_F32>(a, head_dim, group, num_queues, pk, st);
     if (q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_BF16)
-        return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_BF16>(a, head_dim, group, num_queues, uniform, st);
+        return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_BF16>(a, head_dim, group, num_queues, pk, st);
     if (q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_FP8_E4M3)
-        return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3>(a, head_dim, group, num_queues, uniform, st);
+        return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3>(a, head_dim, group, num_queues, pk, st);
     return PKV_ERR_UNSUPPORTED;
 }
 

@@ -147,19 +147,39 @@ __device__ __forceinline__ void token_pairs(uint32_t (&lo)[NP], uint32_t (&hi)[N
 // those lanes to -inf, so their p is exactly 0 and the (finite) clamp values
 // add nothing.  A token on a page outside the pool sets `bad` (its rows are
 // written as NaN) and reads the pool start or the clamp token.
-// Sub-tiles of 16 tokens in a wave-tile of U groups of 4 tokens (pages of a
-// multiple of 16 tokens: one page id per sub-tile).
-template <int U>
-constexpr int kSubTiles = U >= 4 ? U / 4 : 1;
+// How the decode unit finds the page of a key:
+//   kPageTile   pages of a multiple of 16 tokens: one page id per 16-token
+//               sub-tile of a wave-tile;
+//   kPageGroup  pages of 4 or 8 tokens: one page id per group of 4 tokens
+//               (one load instruction's tokens all lie in one page);
+//   kPageOne    one-token pages: each lane reads its tokens' table entries
+//               (vector loads) a wave-tile ahead of their use, and a token's
+//               slot is its page;
+//   kPageAny    any other page size: each lane reads its tokens' table
+//               entries when the tile starts, and divides.
+// Tiles and groups read the page ids of a wave-tile through scalar loads a
+// tile ahead of their use.
+constexpr int kPageAny = 0;
+constexpr int kPageOne = 1;
+constexpr int kPageGroup = 2;
+constexpr int kPageTile = 3;
 
-// Page ids of the sub-tiles of the wave-tile at t0 (-1 past ke or past the
-// table): scalar loads, issued a tile ahead of their use.
-template <int U>
-__device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const AttnArgs& a,
+// Tokens per page id of a wave-tile, and page ids per wave-tile of U groups
+// of 4 tokens.
+template <int PK>
+constexpr int kEntryTokens = PK == kPageOne ? 1 : (PK == kPageGroup ? 4 : 16);
+template <int U, int PK>
+constexpr int kTileEntries =
+    (PK == kPageAny || PK == kPageOne) ? 1 : (4 * U >= kEntryTokens<PK> ? 4 * U / kEntryTokens<PK> : 1);
+
+// Page ids of the wave-tile at t0 (-1 past ke or past the table): scalar
+// loads, issued a tile ahead of their use.
+template <int U, int PK>
+__device__ __forceinline__ void tile_pages(int32_t (&pages)[(kTileEntries<U, PK>)], const AttnArgs& a,
                                            const SeqTable& tbl, int t0, int ke) {
 #pragma unroll
-    for (int s = 0; s < kSubTiles<U>; ++s) {
-        const int ts = t0 + 16 * s;
+    for (int s = 0; s < kTileEntries<U, PK>; ++s) {
+        const int ts = t0 + kEntryTokens<PK> * s;
         const int pidx = page_of(a, ts);
         pages[s] = (ts < ke && pidx < tbl.n) ? tbl[pidx] : -1;
     }
@@ -167,8 +187,7 @@ __device__ __forceinline__ void tile_pages(int32_t (&pages)[kSubTiles<U>], const
 
 // Per-token pages: the table entries of this lane's tokens t0 + 4u + row of
 // the wave-tile at t0 (tokens at or past lim take the piece's last key),
-// read unconditionally at a clamped index.  (Reading them a tile ahead was
-// measured slower on one-token pages.)
+// read unconditionally at a clamped index.
 template <int U>
 __device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, const SeqTable& tbl, int t0,
                                            int lim, int ke, int row) {
@@ -181,21 +200,34 @@ __device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, 
     }
 }
 
-template <int KVDT, int D, int U, int KW, bool UNIFORM_PAGE, bool FULL>
+// Loads of one wave-tile: U groups of 4 tokens (token t0 + 4u + row in lane
+// row `row`).  FULL: every token of the tile is below ke.  Every load is
+// issued, unconditionally, so that the wait before the products can count
+// exactly the loads still in flight: a lane whose token is past the piece
+// reads the unit's clamp token instead (`clamp_off`: the last key of the
+// piece).  The caller masks the scores of those lanes to -inf, so their p is
+// exactly 0 and the (finite) clamp values add nothing.  A token on a page
+// outside the pool sets `bad` (its rows are written as NaN) and reads the
+// pool start or the clamp token.
+//   kPageTile / kPageGroup: the tokens of an entry share a page, so the
+//     entry's base address is scalar and the lane adds a 32-bit offset;
+//   kPageOne: the lane's page is its row's entry; the slot is the page;
+//   kPageAny: the lane's own table entries (lp) and 64-bit slots.
+template <int KVDT, int D, int U, int KW, int PK, bool FULL>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
-                                          const int32_t (&pages)[kSubTiles<U>], const int32_t (&lp)[U],
+                                          const int32_t (&pages)[(kTileEntries<U, PK>)], const int32_t (&lp)[U],
                                           const char* kc, const char* vc, int t0, int ke, int row, uint32_t lane_off,
                                           uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, int tbl_n,
                                           bool& bad) {
     const int bs = a.block_size;
     // block ids are int32: a pool of more than 2^31 - 1 blocks is addressed up to that many
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
-    if constexpr (UNIFORM_PAGE) {
-        constexpr int SUB = kSubTiles<U>;
-        constexpr int PER = U < 4 ? U : 4;
+    if constexpr (PK == kPageTile || PK == kPageGroup) {
+        constexpr int SUB = kTileEntries<U, PK>;
+        constexpr int PER = U / SUB;  // 4-token groups per entry
 #pragma unroll
         for (int s = 0; s < SUB; ++s) {
-            const int ts = t0 + 16 * s;
+            const int ts = t0 + kEntryTokens<PK> * s;
             const int pidx = page_of(a, ts);
             const bool in = FULL || ts < ke;
             const uint32_t page = static_cast<uint32_t>(pages[s]);
@@ -209,7 +241,7 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
             const char* vb = vc + slot0 * tok_bytes;
 #pragma unroll
             for (int uu = 0; uu < PER; ++uu) {
-                const int u = 4 * s + uu;
+                const int u = PER * s + uu;
                 if constexpr (FULL) {
                     // a page outside the pool reads the pool start: its rows come out NaN anyway
                     k[u] = load_words_nt<KW>(kb + 4 * uu * tok_bytes + lane_off);
@@ -221,6 +253,19 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
                     v[u] = load_words_nt<KW>(vc + off);
                 }
             }
+        }
+    } else if constexpr (PK == kPageOne) {
+        // one-token pages: the slot of token t0 + 4u + row is its page (lp)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 4 * u + row;
+            const bool tv = FULL || t < ke;
+            const uint32_t page = static_cast<uint32_t>(lp[u]);
+            const bool ok = tv && t < tbl_n && page < nblocks;  // a negative id wraps to >= 2^31
+            bad |= tv && !ok;
+            const int64_t off = ok ? static_cast<int64_t>(page) * tok_bytes + head_off : clamp_off;
+            k[u] = load_words_nt<KW>(kc + off);
+            v[u] = load_words_nt<KW>(vc + off);
         }
     } else {
         // one page per token: lane row r takes the page of token t0 + 4u + r
@@ -377,8 +422,10 @@ struct DecodeLds {
 // partial with its log-sum-exp at partial row `prow`.  Every wave of the
 // workgroup makes the same calls (flush contains barriers when waves share a
 // head).
-template <int QDT, int KVDT, int D, int G, int NW, bool UNIFORM_PAGE>
+template <int QDT, int KVDT, int D, int G, int NW, int PK>
 struct DecodeRun {
+    // page ids through scalar loads a tile ahead (else per-lane table reads)
+    static constexpr bool UNIFORM_PAGE = PK == kPageTile || PK == kPageGroup;
     using R = DecodeRegs<QDT, KVDT, D, G>;
     static constexpr int EPL = R::EPL;
     static constexpr int KW = R::KW;
@@ -458,25 +505,30 @@ struct DecodeRun {
         // Whole-tile pages: the page ids of the wave's next tile are loaded
         // while this tile is computed, so the next tile's K/V loads need not
         // wait for a table read.
-        int32_t pages[kSubTiles<U>];
+        int32_t pages[(kTileEntries<U, PK>)];
         int32_t lp[U];  // per-token pages: this lane's table entries
-        if constexpr (UNIFORM_PAGE) tile_pages<U>(pages, a, tbl, ta + sub * TT, tb);
+        if constexpr (UNIFORM_PAGE) tile_pages<U, PK>(pages, a, tbl, ta + sub * TT, tb);
+        if constexpr (PK == kPageOne) lane_pages<U>(lp, a, tbl, ta + sub * TT, tb, ke, row);
         const uint32_t vspan = static_cast<uint32_t>(max(tb - lo, 0));  // keys lo .. tb - 1 are valid
         // the loop is built twice, with and without the logit soft-cap, so
         // that the plain call's loop carries no test of it
         auto loop = [&](auto cap_on) {
         for (int t0 = ta + sub * TT; t0 < tb; t0 += step) {
             Words<KW> kr[U], vr[U];
-            if constexpr (!UNIFORM_PAGE) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
+            if constexpr (PK == kPageAny) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
             if (t0 + TT <= tb) {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, true>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
-                                                              head_off, tok_bytes, clamp_off, tbl.n, bad);
+                load_tile<KVDT, D, U, KW, PK, true>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off, head_off,
+                                                    tok_bytes, clamp_off, tbl.n, bad);
             } else {
-                load_tile<KVDT, D, U, KW, UNIFORM_PAGE, false>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
-                                                               head_off, tok_bytes, clamp_off, tbl.n, bad);
+                load_tile<KVDT, D, U, KW, PK, false>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off, head_off,
+                                                     tok_bytes, clamp_off, tbl.n, bad);
             }
             if constexpr (UNIFORM_PAGE) {
-                if (t0 + step < tb) tile_pages<U>(pages, a, tbl, t0 + step, tb);
+                if (t0 + step < tb) tile_pages<U, PK>(pages, a, tbl, t0 + step, tb);
+            }
+            if constexpr (PK == kPageOne) {
+                // the next wave-tile's entries, while this one is computed
+                if (t0 + step < tb) lane_pages<U>(lp, a, tbl, t0 + step, tb, ke, row);
             }
             // lo <= t0 + my_tok < tb as one unsigned compare
             const bool valid = static_cast<uint32_t>(t0 - lo + my_tok) < vspan;
@@ -591,9 +643,9 @@ __device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.prow < 0
 
 // One decode unit, all of it, on the calling workgroup: every kv head, whole
 // units to the output row, pieces to their partial row.
-template <int QDT, int KVDT, int D, int G, int NW, bool UNIFORM_PAGE>
+template <int QDT, int KVDT, int D, int G, int NW, int PK>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, DecodeLds<D, G, NW>& lds) {
-    DecodeRun<QDT, KVDT, D, G, NW, UNIFORM_PAGE> run(a);
+    DecodeRun<QDT, KVDT, D, G, NW, PK> run(a);
     const bool direct = unit_is_whole(un);
     for (int h = run.head0; h < a.hkv; h += run.hstep) {
         run.open(a, un, h);

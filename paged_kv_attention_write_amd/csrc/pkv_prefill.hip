@@ -662,7 +662,7 @@ __device__ __forceinline__ void mixed_decode_queue(const AttnArgs& a, int b, Dec
     const const_ptr<int32_t> qoff = as_const(a.queue_off);
     const int u_end = qoff[b + 1];
     for (int ui = qoff[b]; ui < u_end; ++ui)
-        decode_unit<PKV_DTYPE_BF16, PKV_DTYPE_BF16, D, G, kPfWaves, true>(a, load_unit(units, ui), lds);
+        decode_unit<PKV_DTYPE_BF16, PKV_DTYPE_BF16, D, G, kPfWaves, kPageTile>(a, load_unit(units, ui), lds);
 }
 
 template <int KVDT, int D, int G, bool RING>

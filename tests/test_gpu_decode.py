@@ -44,7 +44,7 @@ def test_decode_workload_full_size(gpu):
     check_close(got, ref, "bf16", f"decode units={plan.desc.num_units} merges={plan.desc.num_merges}")
 
 
-@pytest.mark.parametrize("bs", [1, 3, 4, 7, 16, 32, 48, 64])
+@pytest.mark.parametrize("bs", [1, 2, 3, 4, 7, 8, 16, 32, 48, 64])
 @pytest.mark.parametrize("num_queues", [1, 9, 0])
 def test_block_sizes(gpu, bs, num_queues):
     log(f"block size {bs} queues={num_queues}")
@@ -55,15 +55,18 @@ def test_block_sizes(gpu, bs, num_queues):
     check_close(got, ref, "bf16", f"bs={bs}")
 
 
+@pytest.mark.parametrize("bs", [16, 1, 4])
 @pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (8, 1, 128), (16, 8, 64), (32, 4, 128), (64, 8, 128),
                                       (4, 2, 64)])
-def test_head_shapes(gpu, hq, hkv, d):
-    log(f"heads {hq}/{hkv} d={d}")
+def test_head_shapes(gpu, hq, hkv, d, bs):
+    """Every group size and head_dim on each page kind: whole 16-token tiles,
+    one-token pages, groups of 4 tokens."""
+    log(f"heads {hq}/{hkv} d={d} bs={bs}")
     lens = [5, 300, 77, 1024]
     case = workloads.build_case("heads", 50, lens, [1] * 4, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
-                                block_size=16)
+                                block_size=bs)
     got, ref, _, _ = _run(case, gpu, 7)
-    check_close(got, ref, "bf16", f"heads {hq}/{hkv} d={d}")
+    check_close(got, ref, "bf16", f"heads {hq}/{hkv} d={d} bs={bs}")
 
 
 def test_permutation_and_sharing_are_bit_identical(gpu):
@@ -172,12 +175,13 @@ def test_fp8_prefix_shared_full_size(gpu):
     check_close(got, ref, "fp8", "fp8 prefix")
 
 
+@pytest.mark.parametrize("bs", [16, 1, 4])
 @pytest.mark.parametrize("d", [64, 128])
-def test_fp8_small(gpu, d):
+def test_fp8_small(gpu, d, bs):
     case = workloads.build_case("fp8s", 62, [3, 70, 500, 16], [1] * 4, num_q_heads=16, num_kv_heads=4, head_dim=d,
-                                block_size=16, kv_dtype="fp8")
+                                block_size=bs, kv_dtype="fp8")
     got, ref, _, _ = _run(case, gpu, 6)
-    check_close(got, ref, "fp8", f"fp8 d={d}")
+    check_close(got, ref, "fp8", f"fp8 d={d} bs={bs}")
 
 
 def test_q_token_stride(gpu):
