@@ -372,14 +372,18 @@ def study_pages(args, torch, pkv, workloads, byte_model):
     """Page-size sweep: decode over equal-length batches of the pages' three
     shapes (64 x 4096, 16 x 16384, 256 x 1024 keys), pages of 1, 4, 16 and 64
     tokens in shuffled order and one contiguous slab (page 16 in order), one
-    JSON line per case."""
+    JSON line per case.  The five layouts of a shape are resident together
+    and their calls alternate (the starting layout rotating every step), so
+    that the ratios to the contiguous slab compare calls made under the same
+    conditions."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    layouts = (("contiguous", 16), ("shuffled", 1), ("shuffled", 4), ("shuffled", 16), ("shuffled", 64))
     for batch, n in ((64, 4096), (16, 16384), (256, 1024)):
-        ref_us = None
-        for layout, bs in (("contiguous", 16), ("shuffled", 1), ("shuffled", 4), ("shuffled", 16), ("shuffled", 64)):
-            lens = np.full(batch, n, np.int32)
+        lens = np.full(batch, n, np.int32)
+        cases = []
+        for layout, bs in layouts:
             st = workloads.structure_for_lengths(workloads.CONFIG_IDS["skew"], lens, block_size=bs,
                                                  layout="identity" if layout == "contiguous" else "shuffle")
             layers = build_layers(torch, st, {"config": "decode"}, args.layers, dev)
@@ -387,35 +391,39 @@ def study_pages(args, torch, pkv, workloads, byte_model):
             ctx = torch.from_numpy(st["context_lens"]).to(dev)
             plan = pkv.Plan(lens, None, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
                             num_queues=args.queues)
-            cnt = args.steps * len(layers)
-            ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(cnt)]
-            ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(cnt)]
-            for it in range(args.warmup + args.steps):
-                for l, layer in enumerate(layers):
-                    k = (it - args.warmup) * len(layers) + l
-                    if k >= 0:
-                        ev_a[k].record(stream)
-                    pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan)
-                    if k >= 0:
-                        ev_b[k].record(stream)
-            torch.cuda.synchronize()
-            ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-            nbytes = byte_model.attention_bytes(lens, st["q_lens"], 32, 8, 128, bs, 2, 2)
+            cases.append(dict(layout=layout, bs=bs, st=st, layers=layers, tables=tables, ctx=ctx, plan=plan, ev=[]))
+        for it in range(args.warmup + args.steps):
+            k = it % len(cases)
+            for c in cases[k:] + cases[:k]:
+                for layer in c["layers"]:
+                    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a_.record(stream)
+                    pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], c["tables"], c["ctx"],
+                                          scale, c["plan"])
+                    b_.record(stream)
+                    if it >= args.warmup:
+                        c["ev"].append((a_, b_))
+        torch.cuda.synchronize()
+        ref_us = None
+        for c in cases:
+            ms = np.array([a_.elapsed_time(b_) for a_, b_ in c["ev"]])
+            nbytes = byte_model.attention_bytes(lens, c["st"]["q_lens"], 32, 8, 128, c["bs"], 2, 2)
             p50 = float(np.median(ms)) * 1e-3
-            if layout == "contiguous":
+            if c["layout"] == "contiguous":
                 ref_us = p50
-            cb = pages_cpu_baseline(torch, st, layers[0], scale)
+            cb = pages_cpu_baseline(torch, c["st"], c["layers"][0], scale)
             print(json.dumps({
-                "study": "pages", "batch": batch, "context": n, "layout": layout, "block_size": bs,
-                "table_entries": int(st["block_tables"].size),
+                "study": "pages", "batch": batch, "context": n, "layout": c["layout"], "block_size": c["bs"],
+                "table_entries": int(c["st"]["block_tables"].size),
                 "call_us": {"p10": round(float(np.percentile(ms, 10)) * 1e3, 2), "p50": round(p50 * 1e6, 2),
                             "p90": round(float(np.percentile(ms, 90)) * 1e3, 2)},
                 "TBps": round(nbytes / p50 / 1e12, 4), "frac_of_8TBps": round(nbytes / p50 / 8e12, 4),
-                "vs_contiguous": round(ref_us / p50, 4), "layers": len(layers), "cpu_baseline": cb}), flush=True)
+                "vs_contiguous": round(ref_us / p50, 4), "layers": len(c["layers"]), "cpu_baseline": cb}),
+                  flush=True)
             if not cb["parity"]["ok"]:
-                raise SystemExit(f"page-size sweep: layer 0 differs from the oracle at {layout} page {bs}")
-            del layers, plan, tables
-            torch.cuda.empty_cache()
+                raise SystemExit(f"page-size sweep: layer 0 differs from the oracle at {c['layout']} page {c['bs']}")
+        del cases
+        torch.cuda.empty_cache()
 
 
 def pages_cpu_baseline(torch, st, layer, scale, samples=6):
