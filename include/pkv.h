@@ -327,6 +327,11 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
  * the prefill units are two launches.  So one call is one or two attention
  * launches followed by the merge launch.
  * Same arguments and errors as paged_attn_decode, with the plan made from
+ * A step whose chunks all hold at most 16 (row, q head) pairs per kv head
+ * (at most 16 / G rows: a speculative verify step) is planned as decode rows
+ * are, each unit holding a sequence's rows and every kv head, and runs one
+ * few-row launch (matrix-core tiles, one wave per kv head) and the merge.
+ * Same arguments and errors as paged_attn_decode, with the plan made from
  * the same q_lens, plus: PKV_ERR_NULL for a NULL cu_seqlens with rows to
  * compute, PKV_ERR_UNSUPPORTED when the plan has chunk rows
  * and q is not bf16 (K/V bf16 or fp8; decode-only plans take every dtype
@@ -337,7 +342,7 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
  * ("nanoserve", "Packed batches" and chunked-prefill bullets, and the
  * benchmark note on splitting each mixed step into decode rows and prefill
  * chunks; "How to design an LLM serving system", "Latency and scaling
- * knobs": chunked prefill.)
+ * knobs": chunked prefill and speculative verify.)
  */
 int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_cache,
                      const void* v_cache, int32_t kv_dtype, const int32_t* block_tables,

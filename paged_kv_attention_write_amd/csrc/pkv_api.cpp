@@ -334,7 +334,7 @@ int paged_attn_decode_csr(void* out, const void* q, int32_t q_dtype, int64_t q_t
 
 // Most rows of any merge record: decode merges have one, prefill merges a row block.
 static int merge_rows(const pkv_plan* plan, int group) {
-    if (plan->num_prefill_units == 0) return 1;
+    if (plan->max_q_len <= 1) return 1;
     return std::max(1, std::min(plan->max_q_len, std::max(1, kPrefillQRows / group)));
 }
 
@@ -359,22 +359,33 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
     a.cu_seqlens = cu_seqlens;
     const int group = num_q_heads / num_kv_heads;
     const bool chunks = plan->num_prefill_units > 0;
-    if (chunks && !prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    // the prefill tile stages 8 elements of a key per load
+    // a few-row step: the sequences' rows sit in decode-queue units
+    const bool few = !chunks && plan->max_q_len > 1;
+    if ((chunks || few) && !prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    // the prefill and few-row tiles load 8 elements of a key at a time
     const size_t item = 8 * static_cast<size_t>(dt_bytes(kv_dtype));
-    if (chunks && (!aligned(k_cache, item) || !aligned(v_cache, item))) return PKV_ERR_SHAPE;
-    if (chunks && mixed_one_launch(q_dtype, kv_dtype, head_dim, group, block_size)) {
+    if ((chunks || few) && (!aligned(k_cache, item) || !aligned(v_cache, item))) return PKV_ERR_SHAPE;
+    const bool decode_rows = plan->num_units > plan->num_prefill_units;
+    if (few) {
+        st = launch_fewrow(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
+        if (st != PKV_OK) return st;
+        return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
+    }
+    // decode rows and chunks side by side in one launch; chunks alone take
+    // the prefill kernel, whose wide form needs no room for a decode
+    // workgroup on the CU
+    if (chunks && decode_rows && mixed_one_launch(q_dtype, kv_dtype, head_dim, group, block_size)) {
         st = launch_mixed(a, head_dim, group, plan->num_queues, plan->num_prefill_queues, stream);
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }
-    if (plan->num_units > plan->num_prefill_units) {
+    if (decode_rows) {
         st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
         if (st != PKV_OK) return st;
     }
     if (chunks) {
-        st = launch_prefill(a, q_dtype, kv_dtype, head_dim, group, plan->num_prefill_queues, plan->num_queues,
-                            stream);
+        st = launch_prefill(a, q_dtype, kv_dtype, head_dim, group, plan->max_q_len, plan->num_prefill_queues,
+                            plan->num_queues, stream);
         if (st != PKV_OK) return st;
     }
     return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);

@@ -114,10 +114,16 @@ __device__ __forceinline__ void store_out(char* dst, const float (&o)[EPL]) {
 
 int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream);
-// Prefill chunks: the prefill queues num_queues .. queue0 + num_queues - 1 of the plan.
+// Prefill chunks: the prefill queues queue0 .. queue0 + num_queues - 1 of
+// the plan; max_q_len (the plan's longest chunk) picks the tile width.
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group);
-int launch_prefill(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
-                   int queue0, void* stream);
+int launch_prefill(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int max_q_len,
+                   int num_queues, int queue0, void* stream);
+// A few-row step (every unit on the decode queues, holding a sequence's few
+// rows and every kv head): the few-row kernel, or the register-staged
+// prefill tile where that kernel does not serve the cache.
+int launch_fewrow(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
+                  void* stream);
 // Decode rows and chunks of a mixed step in one launch (bf16 K/V on pages of
 // whole tiles, groups 2 and 4, where one workgroup of each fits a CU).
 bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int block_size);

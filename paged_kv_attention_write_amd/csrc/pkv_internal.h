@@ -25,6 +25,13 @@ constexpr int kPrefillPieceMin = 512;
 // workgroups per CU when the decode launch runs one.
 constexpr int kPrefillQueuesPerQueue = 2;
 
+// A step whose longest chunk has at most this many (row, q head) pairs per
+// kv head (a speculative verify step: a few rows per sequence) is planned as
+// decode rows are: every sequence, whatever its row count, is cut by key
+// tiles over the decode queues, and a unit holds all its rows and every kv
+// head, so that a workgroup streams whole key rows of the pool.
+constexpr int kFewRowPairs = 16;
+
 // Decode queue loads count each piece placed on a queue as this many tiles
 // more than its keys: the set-up of a unit (its first page lookups and
 // loads, its flush) costs about one tile's time, so a queue that runs two
@@ -38,8 +45,9 @@ constexpr int kWideMergeParts = 8;
 
 constexpr size_t kAlign = 256;
 
-// kind == kUnitDecode: a decode unit (one row, every kv head).  kind >= 1: a
-// prefill unit of kv head kind - 1.
+// kind == kUnitDecode: a decode unit (every kv head; one row, or the few
+// rows of a sequence in a few-row step).  kind >= 1: a prefill unit of kv
+// head kind - 1.
 enum UnitKind : int32_t { kUnitDecode = 0, kUnitPrefill = 1 };
 
 // One piece of work: query rows [row0, row0 + nrows) of sequence `seq` (rows

@@ -82,7 +82,9 @@ PlanSections plan_capacity(int64_t max_seqs, int64_t max_tokens, int32_t num_q_h
     c.units = nq + seqs + blocks * kPrefillMaxPieces * hkv;
     c.queue_ints = plan_counts_index(static_cast<int32_t>(nq)) + kPlanCounts;
     c.merges = seqs + blocks;
-    c.prows = nq + seqs + toks * kPrefillMaxPieces;
+    // (a few-row step cuts each sequence by the decode rule: at most
+    // queues - 1 cuts, each adding at most kFewRowPairs rows)
+    c.prows = nq + seqs + toks * kPrefillMaxPieces + nq * kFewRowPairs;
     return c;
 }
 
@@ -133,6 +135,10 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     };
     // flops of one kv head: 2 (q.k) + 2 (p.v) per pair, q head and dimension
     const int64_t flops_per_pair = 4LL * group * head_dim;
+    // a few-row step: every sequence is cut and placed as a decode row is
+    const bool few = max_q > 1 && static_cast<int64_t>(max_q) * group <= kFewRowPairs;
+    // rows a sequence sends through the decode queues
+    auto decode_rows = [&](int32_t L) { return (L == 1 || (few && L > 1)) ? L : 0; };
 
     // Total work and the share per queue.
     int64_t decode_tiles = 0;
@@ -140,8 +146,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int32_t n = ctx[s];
         const int32_t L = q_lens ? q_lens[s] : 1;
-        if (L == 1) decode_tiles += ceil_div(n - range_start(n - 1), kTileTokens);
-        if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
+        if (decode_rows(L) > 0) decode_tiles += ceil_div(n - range_start(n - L), kTileTokens);
+        else if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
     }
     // Decode rows and prefill chunks run as two launches, each balanced on
     // its own queues.
@@ -157,7 +163,7 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     for (int32_t s = 0; s < num_seqs; ++s) {
         const int32_t n = ctx[s];
         const int32_t L = q_lens ? q_lens[s] : 1;
-        if (L <= 1) continue;
+        if (L <= 1 || decode_rows(L) > 0) continue;
         for (int32_t r0 = 0; r0 < L; r0 += block_rows) {
             const int32_t r1 = std::min(L, r0 + block_rows);
             const int32_t nr = r1 - r0;
@@ -223,15 +229,18 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     // Decode requests, longest first, cut to fill the lightest queue.
     std::vector<int32_t> order;
     for (int32_t s = 0; s < num_seqs; ++s)
-        if ((q_lens ? q_lens[s] : 1) == 1 && ctx[s] > 0) order.push_back(s);
-    // keys a decode row reads: from the tile of its first visible key on
-    auto decode_keys = [&](int32_t s) { return ctx[s] - range_start(ctx[s] - 1); };
+        if (decode_rows(q_lens ? q_lens[s] : 1) > 0 && ctx[s] > 0) order.push_back(s);
+    auto rows_of = [&](int32_t s) { return q_lens ? q_lens[s] : 1; };
+    // keys the rows of a request read: from the tile of its first row's
+    // first visible key on
+    auto decode_keys = [&](int32_t s) { return ctx[s] - range_start(ctx[s] - rows_of(s)); };
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t a, int32_t b) { return decode_keys(a) > decode_keys(b); });
     std::vector<std::pair<int32_t, size_t>> placed;  // (queue, index) of the pieces of one request
     for (int32_t s : order) {
         const int32_t n = ctx[s];
-        const int64_t start = range_start(n - 1);
+        const int32_t L = rows_of(s);
+        const int64_t start = range_start(n - L);
         int64_t remaining = ceil_div(n - start, kTileTokens);
         int64_t first = 0;
         placed.clear();
@@ -244,19 +253,21 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
             const int64_t take = room > 0 ? std::min(remaining, room) : remaining;
             const int32_t kb = static_cast<int32_t>(start + first * kTileTokens);
             const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, start + (first + take) * kTileTokens));
-            queues[q].push_back(Unit{s, kb, ke, row0[s], 1, n - 1, -1, kUnitDecode});
+            queues[q].push_back(Unit{s, kb, ke, row0[s], L, n - L, -1, kUnitDecode});
             placed.emplace_back(q, queues[q].size() - 1);
             heap.push(load + take + kDecodeUnitCost, q);
             remaining -= take;
             first += take;
         }
         if (placed.size() > 1) {
+            // piece c's rows at prow0 + c L; a request of several rows merges
+            // as a row block
             const int32_t prow0 = static_cast<int32_t>(partial_rows);
             for (size_t c = 0; c < placed.size(); ++c)
-                queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c);
+                queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c) * L;
             const int32_t parts = static_cast<int32_t>(placed.size());
-            merges.emplace_back(parts >= kWideMergeParts ? 0 : 2, Merge{row0[s], 1, prow0, parts});
-            partial_rows += static_cast<int64_t>(placed.size());
+            merges.emplace_back(L > 1 ? 1 : parts >= kWideMergeParts ? 0 : 2, Merge{row0[s], L, prow0, parts});
+            partial_rows += static_cast<int64_t>(placed.size()) * L;
         }
     }
 

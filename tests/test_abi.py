@@ -376,9 +376,10 @@ def _prefill_queue_costs(lens, ql, nq=256):
 def test_prefill_units_are_balanced():
     """The prefill queues' visible (row, key) pairs stay within 15 % of their
     mean for a 512-row chunk over 2560 keys, and within 10 % for 64
-    sequences of 4 speculative rows over U[512, 4096] keys: chunk row blocks
-    are cut to the nearest count of queue shares, small row blocks 3x finer,
-    and the units are placed largest first by their exact flops."""
+    sequences of 8 rows over U[512, 4096] keys (32 pairs per kv head, past
+    the few-row rule): chunk row blocks are cut to the nearest count of queue
+    shares, small row blocks 3x finer, and the units are placed largest first
+    by their exact flops."""
     import workloads
 
     st = workloads.structure_only("mixed", "page16")
@@ -386,5 +387,36 @@ def test_prefill_units_are_balanced():
     c = _prefill_queue_costs(st["context_lens"][chunk], st["q_lens"][chunk])
     assert c.max() <= 1.15 * c.mean(), c.max() / c.mean()
     lens = workloads.structure_only("decode", "page16")["context_lens"]
-    c = _prefill_queue_costs(lens, np.full(lens.shape[0], 4, np.int32))
+    c = _prefill_queue_costs(lens, np.full(lens.shape[0], 8, np.int32))
     assert c.max() <= 1.1 * c.mean(), c.max() / c.mean()
+
+
+@pytest.mark.parametrize("group,rows", [(4, 4), (1, 16), (8, 2), (2, 8), (4, 3)])
+def test_few_row_step_is_planned_as_decode_rows(group, rows):
+    """A step whose longest chunk holds at most 16 (row, q head) pairs per kv
+    head (a speculative verify step) is cut and placed as decode rows are:
+    its decode queues equal the oracle's split-KV plan over the sequences'
+    keys, each unit holds all rows of its sequence and every kv head, and a
+    cut sequence of several rows merges as a row block with piece c's rows at
+    prow0 + c * rows.  Past 16 pairs the chunks are planned as chunk units.""" 
+    import workloads
+
+    lens = workloads.structure_only("decode", "page16")["context_lens"]
+    hkv, nq = 8, 256
+    ql = np.full(lens.shape[0], rows, np.int32)
+    ql[::5] = 1  # plain decode rows among them
+    p, image = pkv.plan_host(lens, ql, hkv * group, hkv, 128, nq)
+    assert p.num_prefill_units == 0 and p.num_prefill_queues == 0 and p.max_q_len == rows
+    units, qoff, merges = pkv.decode_plan_image(p, image)
+    got = [[(int(u[0]), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]] for q in range(nq)]
+    assert got == split_kv_plan(lens.tolist(), nq, unit_cost=1)
+    cu = np.concatenate([[0], np.cumsum(ql)])
+    for seq, kb, ke, row0, nrows, pos0, prow, kind in units.tolist():
+        assert kind == 0 and nrows == ql[seq] and row0 == cu[seq] and pos0 == lens[seq] - ql[seq]
+    for row0, nrows, prow0, parts in merges.tolist():
+        seq = int(np.searchsorted(cu, row0, side="right") - 1)
+        assert nrows == ql[seq]
+        mine = units[units[:, 0] == seq]
+        assert sorted(mine[:, 6].tolist()) == [prow0 + c * nrows for c in range(parts)]
+    past = np.where(ql > 1, 16 // group + 1, 1).astype(np.int32)
+    assert pkv.plan_host(lens, past, hkv * group, hkv, 128, nq)[0].num_prefill_units > 0

@@ -81,6 +81,10 @@ def _check_plan(p, image, lens, ql, hq, hkv, window):
     units, qoff, merges = pkv.decode_plan_image(p, image)
     cu = np.concatenate([[0], np.cumsum(ql)])
     assert p.num_tokens == cu[-1] and p.num_units == len(units)
+    # a few-row step: every chunk within 16 (row, q head) pairs per kv head
+    few = int(ql.max(initial=0)) > 1 and int(ql.max()) * (hq // hkv) <= 16
+    if few:
+        assert p.num_prefill_units == 0
     assert qoff[0] == 0 and qoff[-1] == p.num_units and np.all(np.diff(qoff) >= 0)
     nq = p.num_queues
     # decode units on decode queues, prefill units on prefill queues
@@ -107,7 +111,9 @@ def _check_plan(p, image, lens, ql, hq, hkv, window):
         if n == 0 or L == 0:
             assert len(mine) == 0
             continue
-        heads = hkv if L > 1 else 1
+        # a chunk unit holds one kv head; decode units (one row, or the few
+        # rows of a few-row step) every kv head
+        heads = hkv if L > 1 and not few else 1
         cover = np.zeros((heads, L, n), np.int32)
         for u in mine:
             seq, kb, ke, row0, nrows, pos0, prow, k = (int(x) for x in u)
@@ -155,6 +161,37 @@ def test_random_batches(seed):
     assert np.array_equal(uc, u0) and np.array_equal(qc, q0) and np.array_equal(mc, m0)
     ws, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
     assert pkv.lib().paged_attn_workspace_size(cap_seqs, cap_tokens, hq, d, nq, ctypes.byref(ws),
+                                               ctypes.byref(host)) == 0
+    assert pc.workspace_bytes <= ws.value and pc.image_bytes <= host.value
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_few_row_batches(seed):
+    """Few-row steps (every sequence with at most 16 / G rows, some with one):
+    planned through the decode queues, every visible pair once, the capacity
+    layout and the workspace bound as for any plan."""
+    rng = np.random.default_rng(2000 + seed)
+    B = int(rng.integers(1, 80))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    lens = rng.integers(0, 5000, size=B)
+    ql = rng.integers(1, 16 // g + 1, size=B)
+    ql = np.minimum(ql, lens)
+    ql[(lens > 0) & (ql == 0)] = 1
+    lens, ql = lens.astype(np.int32), ql.astype(np.int32)
+    nq = int(rng.integers(1, 300))
+    window = int(rng.choice([0, 0, 1, 17, 300]))
+    p, image = pkv.plan_host(lens, ql, hkv * g, hkv, 128, nq, window=window)
+    if int(ql.max(initial=0)) > 1:
+        assert p.num_prefill_units == 0 and p.num_prefill_queues == 0
+    _check_plan(p, image, lens, ql, hkv * g, hkv, window)
+    cap_seqs, cap_tokens = B + 3, int(ql.sum()) + 5
+    pc, imc = _capacity_plan(lens, ql, hkv * g, hkv, 128, nq, window, cap_seqs, cap_tokens)
+    uc, qc, mc = pkv.decode_plan_image(pc, imc)
+    u0, q0, m0 = pkv.decode_plan_image(p, image)
+    assert np.array_equal(uc, u0) and np.array_equal(qc, q0) and np.array_equal(mc, m0)
+    ws, host = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert pkv.lib().paged_attn_workspace_size(cap_seqs, cap_tokens, hkv * g, 128, nq, ctypes.byref(ws),
                                                ctypes.byref(host)) == 0
     assert pc.workspace_bytes <= ws.value and pc.image_bytes <= host.value
 
