@@ -30,7 +30,13 @@ Readings of what the illustration leaves open:
   (the set-up of a unit of work: its first table reads and loads, its
   flush), and the target grows by that much per queue.  0 is the page's
   reading; the library plans with 1, the set-up time of a unit it measured
-  as about one tile's.
+  as about one tile's.  Cutting makes more pieces than queues; if their
+  set-up overflows the target (the lightest queue has no room while a
+  request still has tiles, so it would take the whole rest), the target is
+  raised to ``ceil((total + unit_cost * pieces) / num_queues)`` (at least one
+  more) and every request is placed again, at most 4 placements in all.
+  With ``unit_cost == 0`` the target always holds the total and one
+  placement is made.
 
 ``split_kv_plan`` returns a list of queues; each queue is a list of
 ``(request, kv_begin, kv_end)`` token ranges in the order they were placed.
@@ -58,21 +64,30 @@ def split_kv_plan(kv_lens, num_queues: int, tile: int = TILE_TOKENS, unit_cost: 
     if total == 0:
         return queues
     target = -(-(total + unit_cost * num_queues) // num_queues)
-    loads = [0] * num_queues
     order = sorted(range(len(lens)), key=lambda r: (-lens[r], r))
-    for r in order:
-        remaining = tiles[r]
-        first_tile = 0
-        while remaining > 0:
-            lightest = min(range(num_queues), key=lambda q: (loads[q], q))
-            room = target - loads[lightest] - unit_cost
-            take = min(remaining, room) if room > 0 else remaining
-            begin = first_tile * tile
-            end = min(lens[r], (first_tile + take) * tile)
-            queues[lightest].append((r, begin, end))
-            loads[lightest] += take + unit_cost
-            remaining -= take
-            first_tile += take
+    for attempt in range(4):
+        queues = [[] for _ in range(num_queues)]
+        loads = [0] * num_queues
+        pieces = 0
+        over = False
+        for r in order:
+            remaining = tiles[r]
+            first_tile = 0
+            while remaining > 0:
+                lightest = min(range(num_queues), key=lambda q: (loads[q], q))
+                room = target - loads[lightest] - unit_cost
+                over = over or room <= 0
+                take = min(remaining, room) if room > 0 else remaining
+                begin = first_tile * tile
+                end = min(lens[r], (first_tile + take) * tile)
+                queues[lightest].append((r, begin, end))
+                loads[lightest] += take + unit_cost
+                remaining -= take
+                first_tile += take
+                pieces += 1
+        if not over or unit_cost == 0:
+            break
+        target = max(target + 1, -(-(total + unit_cost * pieces) // num_queues))
     return queues
 
 

@@ -37,6 +37,9 @@ constexpr int kFewRowPairs = 16;
 // loads, its flush) costs about one tile's time, so a queue that runs two
 // pieces is given about a tile less.
 constexpr int kDecodeUnitCost = 1;
+// Placements of the decode requests at most (the share raised after each
+// that overflows it).
+constexpr int kDecodeShareAttempts = 4;
 
 // Alignment of the sections of the workspace.
 // A one-row merge record with at least this many pieces is "wide": its

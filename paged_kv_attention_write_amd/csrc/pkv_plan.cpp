@@ -10,7 +10,8 @@
 // only where a queue fills up (at most queues + requests pieces in all).
 // Every piece also counts one tile of set-up in its queue's load (and the
 // share includes one per queue), so a queue running two pieces gets about
-// one tile less.
+// one tile less; when the cuts make more set-up than the share leaves room
+// for, the share is raised to cover it and the requests are placed again.
 //
 // Query chunks (more than one new row) are split into blocks of rows, one
 // unit per (row block, kv head, key piece), and run as a launch of their own
@@ -219,13 +220,6 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         }
     }
 
-    // The decode share: the decode tiles and a unit's set-up per queue, over
-    // the queues.
-    const int64_t target =
-        decode_tiles > 0 ? ceil_div(decode_tiles + static_cast<int64_t>(kDecodeUnitCost) * num_queues, num_queues) : 0;
-    std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
-    QueueHeap heap(num_queues);
-
     // Decode requests, longest first, cut to fill the lightest queue.
     std::vector<int32_t> order;
     for (int32_t s = 0; s < num_seqs; ++s)
@@ -236,39 +230,64 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     auto decode_keys = [&](int32_t s) { return ctx[s] - range_start(ctx[s] - rows_of(s)); };
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t a, int32_t b) { return decode_keys(a) > decode_keys(b); });
+
+    // The decode share: the decode tiles and a unit's set-up per queue, over
+    // the queues.  Cutting makes more units than queues, and when their
+    // set-up no longer fits the share (a lightest queue with no room while a
+    // request still has tiles) the share is raised to cover the units of
+    // that cut and the requests are placed again: taking the rest on that
+    // queue would leave it up to twice as long as the others.
+    int64_t target =
+        decode_tiles > 0 ? ceil_div(decode_tiles + static_cast<int64_t>(kDecodeUnitCost) * num_queues, num_queues) : 0;
+    std::vector<std::vector<Unit>> queues(static_cast<size_t>(num_queues));
+    const size_t merges0 = merges.size();
+    const int64_t partial_rows0 = partial_rows;
     std::vector<std::pair<int32_t, size_t>> placed;  // (queue, index) of the pieces of one request
-    for (int32_t s : order) {
-        const int32_t n = ctx[s];
-        const int32_t L = rows_of(s);
-        const int64_t start = range_start(n - L);
-        int64_t remaining = ceil_div(n - start, kTileTokens);
-        int64_t first = 0;
-        placed.clear();
-        while (remaining > 0) {
-            auto [load, q] = heap.pop();
-            // what the lightest queue can still take after a unit's set-up;
-            // a full lightest queue (never reached while a queue is below the
-            // share) takes the rest instead of looping
-            const int64_t room = target - load - kDecodeUnitCost;
-            const int64_t take = room > 0 ? std::min(remaining, room) : remaining;
-            const int32_t kb = static_cast<int32_t>(start + first * kTileTokens);
-            const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, start + (first + take) * kTileTokens));
-            queues[q].push_back(Unit{s, kb, ke, row0[s], L, n - L, -1, kUnitDecode});
-            placed.emplace_back(q, queues[q].size() - 1);
-            heap.push(load + take + kDecodeUnitCost, q);
-            remaining -= take;
-            first += take;
+    for (int attempt = 0;; ++attempt) {
+        for (auto& q : queues) q.clear();
+        merges.resize(merges0);
+        partial_rows = partial_rows0;
+        QueueHeap heap(num_queues);
+        int64_t units = 0;
+        bool over = false;
+        for (int32_t s : order) {
+            const int32_t n = ctx[s];
+            const int32_t L = rows_of(s);
+            const int64_t start = range_start(n - L);
+            int64_t remaining = ceil_div(n - start, kTileTokens);
+            int64_t first = 0;
+            placed.clear();
+            while (remaining > 0) {
+                auto [load, q] = heap.pop();
+                // what the lightest queue can still take after a unit's
+                // set-up; with no room left anywhere it takes the rest (and
+                // the share is raised for the next attempt)
+                const int64_t room = target - load - kDecodeUnitCost;
+                over |= room <= 0;
+                const int64_t take = room > 0 ? std::min(remaining, room) : remaining;
+                const int32_t kb = static_cast<int32_t>(start + first * kTileTokens);
+                const int32_t ke = static_cast<int32_t>(std::min<int64_t>(n, start + (first + take) * kTileTokens));
+                queues[q].push_back(Unit{s, kb, ke, row0[s], L, n - L, -1, kUnitDecode});
+                placed.emplace_back(q, queues[q].size() - 1);
+                heap.push(load + take + kDecodeUnitCost, q);
+                remaining -= take;
+                first += take;
+                ++units;
+            }
+            if (placed.size() > 1) {
+                // piece c's rows at prow0 + c L; a request of several rows
+                // merges as a row block
+                const int32_t prow0 = static_cast<int32_t>(partial_rows);
+                for (size_t c = 0; c < placed.size(); ++c)
+                    queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c) * L;
+                const int32_t parts = static_cast<int32_t>(placed.size());
+                merges.emplace_back(L > 1 ? 1 : parts >= kWideMergeParts ? 0 : 2, Merge{row0[s], L, prow0, parts});
+                partial_rows += static_cast<int64_t>(placed.size()) * L;
+            }
         }
-        if (placed.size() > 1) {
-            // piece c's rows at prow0 + c L; a request of several rows merges
-            // as a row block
-            const int32_t prow0 = static_cast<int32_t>(partial_rows);
-            for (size_t c = 0; c < placed.size(); ++c)
-                queues[placed[c].first][placed[c].second].prow = prow0 + static_cast<int32_t>(c) * L;
-            const int32_t parts = static_cast<int32_t>(placed.size());
-            merges.emplace_back(L > 1 ? 1 : parts >= kWideMergeParts ? 0 : 2, Merge{row0[s], L, prow0, parts});
-            partial_rows += static_cast<int64_t>(placed.size()) * L;
-        }
+        if (!over || kDecodeUnitCost == 0 || attempt >= kDecodeShareAttempts - 1) break;
+        target = std::max(target + 1,
+                          ceil_div(decode_tiles + static_cast<int64_t>(kDecodeUnitCost) * units, num_queues));
     }
 
     // merge records: wide ones, then row blocks, then the other one-row

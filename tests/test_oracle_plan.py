@@ -40,8 +40,9 @@ def test_worked_example():
 
 
 def test_worked_example_with_unit_cost():
-    """One tile of set-up per piece, including a request placed when every
-    queue is already full (the lightest one takes it)."""
+    """One tile of set-up per piece, including a first placement whose
+    set-up overflows the target (every queue full while a request has
+    tiles), so the target is raised and the requests are placed again."""
     lens, nq, rows = _golden("plan_unit_cost_example.txt")
     queues = split_kv_plan(lens, nq, unit_cost=1)
     got = [(q, r, b, e) for q, items in enumerate(queues) for (r, b, e) in items]
@@ -52,25 +53,25 @@ def test_worked_example_with_unit_cost():
 @pytest.mark.parametrize("nq", [1, 3, 16, 256])
 def test_unit_cost_covers_once_and_bounds_loads(seed, nq):
     """With set-up per piece: every token covered once in tile-aligned
-    pieces; every queue's load (tiles + one per piece) stays within the
-    target, except a queue that took a rest when every queue was full, which
-    goes over by at most that rest plus its set-up; zero set-up is the
-    page's reading."""
+    pieces; every queue's load (tiles + one per piece) stays within one
+    tile of the balanced share ceil((tiles + pieces) / queues) of the plan
+    made (the target is raised when the set-up overflows it, so no queue
+    takes a whole rest); zero set-up is the page's reading."""
     rng = np.random.default_rng(90 + seed)
     lens = [int(x) for x in rng.integers(0, 3000, size=int(rng.integers(1, 70)))]
     assert split_kv_plan(lens, nq, unit_cost=0) == split_kv_plan(lens, nq)
     queues = split_kv_plan(lens, nq, unit_cost=1)
     tiles = split_lengths(lens)
-    target = -(-(sum(tiles) + nq) // nq) if sum(tiles) else 0
+    pieces = sum(len(items) for items in queues)
+    share = -(-(sum(tiles) + pieces) // nq)
     spans = {r: [] for r in range(len(lens))}
-    biggest = max(tiles) if tiles else 0
     for items in queues:
         load = 0
         for r, b, e in items:
             assert b % TILE_TOKENS == 0 and (e % TILE_TOKENS == 0 or e == lens[r])
             load += -(-(e - b) // TILE_TOKENS) + 1
             spans[r].append((b, e))
-        assert load <= target + biggest + 1
+        assert load <= share + 1
     for r, sp in spans.items():
         sp.sort()
         pos = 0
