@@ -267,7 +267,15 @@ static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_toke
                            context_lens, num_q_heads, num_kv_heads, num_blocks, block_size, scale, k_scale, v_scale,
                            plan, workspace);
     a.kv_indptr = kv_indptr;
-    st = launch_decode(a, q_dtype, kv_dtype, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+    const int group = num_q_heads / num_kv_heads;
+    // fp8 caches: the few-row kernel (products on the matrix cores, the
+    // widening done once as a tile is staged) instead of the vector decode
+    // unit, whose widening and dot products bound it
+    if (kv_dtype == PKV_DTYPE_FP8_E4M3 && fewrow_capable(q_dtype, kv_dtype, head_dim, block_size) &&
+        prefill_supported(q_dtype, kv_dtype, head_dim, group))
+        st = launch_fewrow(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
+    else
+        st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
     if (st != PKV_OK) return st;
     return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
 }

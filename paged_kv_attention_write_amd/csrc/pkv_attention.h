@@ -120,8 +120,11 @@ bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 int launch_prefill(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int max_q_len,
                    int num_queues, int queue0, void* stream);
 // A few-row step (every unit on the decode queues, holding a sequence's few
-// rows and every kv head): the few-row kernel, or the register-staged
-// prefill tile where that kernel does not serve the cache.
+// rows and every kv head): the few-row kernel (bf16 q, bf16 or fp8 K/V,
+// D = 128, pages of a power of two >= 16 tokens: fewrow_capable), or the
+// register-staged prefill tile where that kernel does not serve the cache.
+// The few-row kernel also runs decode calls on fp8 caches.
+bool fewrow_capable(int q_dtype, int kv_dtype, int head_dim, int block_size);
 int launch_fewrow(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream);
 // Decode rows and chunks of a mixed step in one launch (bf16 K/V on pages of

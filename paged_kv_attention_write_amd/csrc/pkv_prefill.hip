@@ -274,15 +274,12 @@ struct RingTile {
 // of a max tree, a packed bf16 conversion and a dot2 into the row sum.  The
 // first VH blocks of the V operand are read before the softmax so that the
 // reads overlap it.
-template <int D, int PB, int VH, class Tile>
-__device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, const int (&pos)[PB], int win,
-                                           const bool (&row_ok)[PB], bool mask, int n, int g4, float qk, float cap,
-                                           float cap_k, const bf16x8_t (&qb)[PB][D / 32], f32x4_t (&acc)[PB][D / 16],
-                                           float (&m_run)[PB], float (&l_run)[PB]) {
+// The first product of a tile: the raw q.k of the wave's pairs (sv[pb][j]:
+// key t0 + 16 (j / 4) + 4 g4 + j % 4 of pair n of block pb).
+template <int D, int PB, class Tile>
+__device__ __forceinline__ void pf_scores(const Tile& T, int n, int g4, const bf16x8_t (&qb)[PB][D / 32],
+                                          float (&sv)[PB][8]) {
     constexpr int NS = D / 32;
-    constexpr int ND = D / 16;
-    const uint16_t* const vl = T.v_lane(n, g4);
-    float sv[PB][8];  // raw q.k
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
         f32x4_t c[PB];
@@ -300,6 +297,17 @@ __device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, cons
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[pb][4 * kb2 + i] = c[pb][i];
     }
+}
+
+// The rest of a tile from its raw scores: soft-cap, mask, online softmax and
+// O^T += V^T P^T.
+template <int D, int PB, int VH, class Tile>
+__device__ __forceinline__ void pf_update(const Tile& T, float (&sv)[PB][8], int t0, int kend,
+                                          const int (&pos)[PB], int win, const bool (&row_ok)[PB], bool mask, int n,
+                                          int g4, float qk, float cap, float cap_k, f32x4_t (&acc)[PB][D / 16],
+                                          float (&m_run)[PB], float (&l_run)[PB]) {
+    constexpr int ND = D / 16;
+    const uint16_t* const vl = T.v_lane(n, g4);
     if (cap > 0.f) {  // capped scores are already in log2 units
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
@@ -374,6 +382,16 @@ __device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, cons
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
             acc[pb][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[b], pbv[pb], acc[pb][b], 0, 0, 0);
+}
+
+template <int D, int PB, int VH, class Tile>
+__device__ __forceinline__ void pf_compute(const Tile& T, int t0, int kend, const int (&pos)[PB], int win,
+                                           const bool (&row_ok)[PB], bool mask, int n, int g4, float qk, float cap,
+                                           float cap_k, const bf16x8_t (&qb)[PB][D / 32], f32x4_t (&acc)[PB][D / 16],
+                                           float (&m_run)[PB], float (&l_run)[PB]) {
+    float sv[PB][8];
+    pf_scores<D, PB>(T, n, g4, qb, sv);
+    pf_update<D, PB, VH>(T, sv, t0, kend, pos, win, row_ok, mask, n, g4, qk, cap, cap_k, acc, m_run, l_run);
 }
 
 // One wave's share of a prefill unit: its PB blocks of 16 (row, q head)
@@ -692,13 +710,13 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
         e[3] = entries(kb + 3 * kPfKeys);
         e[0] = entries(kb + 4 * kPfKeys);
 
-        // tile tt from stage cur; tile tt + 3 into stage nxt with entry
-        // use_e; the entry of tile tt + 5 into load_e
-        auto phase = [&](int tt, uint16_t* cur, uint16_t* nxt, Entries use_e, Entries& load_e) {
+        // this wave's loads of tile tt are in once at most those of the
+        // `later` tiles issued after it are still in flight; keys at or
+        // past kend were read from inside their page (or from the last
+        // group): their V rows are zeroed so that a zero weight never meets
+        // a non-finite value
+        auto land = [&](int tt, uint16_t* st, int later) {
             const int t0 = kb + tt * kPfKeys;
-            // this wave's loads of tile tt are in once at most those of the
-            // (up to two) later tiles already issued are still in flight
-            const int later = min(2, ntiles - 1 - tt);
             if (later >= 2)
                 wait_vmcnt<4 * SE>();
             else if (later == 1)
@@ -706,20 +724,24 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
             else
                 wait_vmcnt<0>();
             if (t0 + kPfKeys > kend) {
-                // keys at or past kend were read from inside their page (or
-                // from the last group): zero their V rows so that a zero
-                // weight never meets a non-finite value
                 if (j >= 2) {
 #pragma unroll
                     for (int f = 0; f < 2; ++f)
 #pragma unroll
                         for (int e = 0; e < SE; ++e)
                             if (t0 + 16 * f + wave + NWV * e + 8 * (j & 1) >= kend)
-                                *reinterpret_cast<uint4*>(cur + (8 * f + wave + NWV * e) * kRingSlotElems + lane * 8) =
+                                *reinterpret_cast<uint4*>(st + (8 * f + wave + NWV * e) * kRingSlotElems + lane * 8) =
                                     make_uint4(0, 0, 0, 0);
                 }
                 wait_lgkmcnt0();
             }
+        };
+        // tile tt from stage cur; tile tt + 3 into stage nxt with entry
+        // use_e; the entry of tile tt + 5 into load_e
+        auto phase = [&](int tt, uint16_t* cur, uint16_t* nxt, Entries use_e, Entries& load_e) {
+            const int t0 = kb + tt * kPfKeys;
+            // the (up to two) later tiles already issued may stay in flight
+            land(tt, cur, min(2, ntiles - 1 - tt));
             ring_barrier();
             if (tt + 3 < ntiles) issue(nxt, t0 + 3 * kPfKeys, use_e);
             load_e = entries(t0 + 5 * kPfKeys);
@@ -797,19 +819,36 @@ void prefill_wide_kernel(AttnArgs a, int queue0) {
 // ---------------------------------------------------------------------------
 constexpr int kFrWaves = 8;
 
-// Registers of one tile in flight: the lane's 16 bytes of each of the 16
-// slots of the ring layout (row lane / 16 of slot 8 f + i: the K row (rows 0
-// and 1) or V row (rows 2 and 3) of key 16 f + i + 8 (row % 2), stored chunk
-// lane % 16).
+// Registers of one tile in flight: the lane's piece of each of the 16 slots
+// of the ring layout (row lane / 16 of slot 8 f + i: the K row (rows 0 and
+// 1) or V row (rows 2 and 3) of key 16 f + i + 8 (row % 2), stored chunk
+// lane % 16): 16 bytes of bf16, or the 8 fp8 codes that widen to them.
+template <int KVDT>
 struct FrRegs {
-    u32x4_t x[16];
+    using piece_t = std::conditional_t<KVDT == PKV_DTYPE_FP8_E4M3, u32x2_t, u32x4_t>;
+    piece_t x[16];
 };
 
+// A slot piece as 8 bf16 values (fp8 E4M3 codes widen exactly: low and high
+// code pairs of each word).
+__device__ __forceinline__ u32x4_t fr_bf16(const u32x4_t& x) { return x; }
+__device__ __forceinline__ u32x4_t fr_bf16(const u32x2_t& x) {
+    auto lo = [](uint32_t d) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(d), 1.0f, false));
+    };
+    auto hi = [](uint32_t d) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(d), 1.0f, true));
+    };
+    return u32x4_t{lo(x.x), hi(x.x), lo(x.y), hi(x.y)};
+}
+
 // Unit `un`, kv head h, on the calling wave alone; st is the wave's tile.
-template <int G>
+template <int KVDT, int G>
 __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, int h, uint16_t* st, int lane) {
     constexpr int D = 128;
-    constexpr int RB = D * 2;  // bytes of one key's row of one kv head
+    constexpr int RB = D * dt_bytes(KVDT);  // bytes of one key's row of one kv head
+    constexpr int PIECE = RB / 16;          // bytes of a lane's piece of a row
+    using Regs = FrRegs<KVDT>;
     const int j = lane >> 4;   // slot row of this lane
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     const int shift = a.block_shift;
@@ -817,7 +856,7 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     // this lane's source in slot i of a half: key i + 8 (j % 2) of the half,
     // K (j < 2) or V, logical chunk (lane % 16) ^ (j % 2)
     const char* const src = static_cast<const char*>(j < 2 ? a.k_cache : a.v_cache) + (8 * (j & 1)) * row_bytes +
-                            static_cast<uint32_t>(((lane & 15) ^ (j & 1)) * 16);
+                            static_cast<uint32_t>(((lane & 15) ^ (j & 1)) * PIECE);
 
     // the unit's pairs as "wave 0" of a layout of one pair block per wave
     PfWave<D, G, kPfWaves, 1> W;
@@ -834,7 +873,7 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     // not there is one, so that the compiler counts the loads in flight
     // exactly at every wait) they read the first rows of the pool (a few
     // KiB, cached) and are never used.
-    auto issue = [&](int i, FrRegs& r) {
+    auto issue = [&](int i, Regs& r) {
         const int t0 = kb + kPfKeys * i;
         const bool live = i < ntiles;
 #pragma unroll
@@ -848,7 +887,8 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
             const char* const base = src + (row0 * a.hkv + h) * RB;
 #pragma unroll
             for (int i8 = 0; i8 < 8; ++i8)
-                r.x[8 * f + i8] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + i8 * row_bytes));
+                r.x[8 * f + i8] = __builtin_nontemporal_load(
+                    reinterpret_cast<const typename Regs::piece_t*>(base + i8 * row_bytes));
         }
     };
     // tile c into the wave's LDS tile; V rows of keys at or past kend were
@@ -856,18 +896,18 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     // zeros, so that a zero weight never meets a non-finite value (the
     // previous tile's reads of the LDS tile have completed: they are waited
     // for where they are issued)
-    auto stage = [&](int c, const FrRegs& r) {
+    auto stage = [&](int c, const Regs& r) {
         const int t0 = kb + kPfKeys * c;
 #pragma unroll
         for (int s16 = 0; s16 < 16; ++s16) {
             const bool zero = j >= 2 && t0 + 16 * (s16 >> 3) + (s16 & 7) + 8 * (j & 1) >= kend;
             *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) =
-                zero ? u32x4_t{0u, 0u, 0u, 0u} : r.x[s16];
+                zero ? u32x4_t{0u, 0u, 0u, 0u} : fr_bf16(r.x[s16]);
         }
     };
 
     // one register set: a tile's registers are free once it is in LDS
-    FrRegs r;
+    Regs r;
     issue(0, r);
     for (int c = 0; c < ntiles; ++c) {
         stage(c, r);
@@ -886,7 +926,7 @@ void fewrow_reg_kernel(AttnArgs a) {
     prefill_queue<KVDT, D, G, true>(a, blockIdx.x, lds);
 }
 
-template <int G>
+template <int KVDT, int G>
 __global__ __launch_bounds__(kFrWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void fewrow_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[kFrWaves * kRingStageElems];
@@ -898,7 +938,7 @@ void fewrow_kernel(AttnArgs a) {
     const int u_end = qoff[blockIdx.x + 1];
     for (int ui = qoff[blockIdx.x]; ui < u_end; ++ui) {
         const Unit un = load_unit(units, ui);
-        for (int h = wave; h < a.hkv; h += kFrWaves) fewrow_head<G>(a, un, h, st, lane);
+        for (int h = wave; h < a.hkv; h += kFrWaves) fewrow_head<KVDT, G>(a, un, h, st, lane);
     }
 }
 
@@ -1015,20 +1055,30 @@ int launch_mixed_d(const AttnArgs& a, int d, int group, int num_decode_queues, i
 
 }  // namespace
 
+bool fewrow_capable(int q_dtype, int kv_dtype, int head_dim, int block_size) {
+    return q_dtype == PKV_DTYPE_BF16 && (kv_dtype == PKV_DTYPE_BF16 || kv_dtype == PKV_DTYPE_FP8_E4M3) &&
+           head_dim == 128 && block_size >= kTileTokens && (block_size & (block_size - 1)) == 0;
+}
+
 int launch_fewrow(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!prefill_supported(q_dtype, kv_dtype, head_dim, group)) return PKV_ERR_UNSUPPORTED;
     const dim3 grid(num_queues);
-    if (kv_dtype == PKV_DTYPE_BF16 && head_dim == 128 && ring_pages(a)) {
-        switch (group) {
-            case 1: hipLaunchKernelGGL((fewrow_kernel<1>), grid, dim3(kFrWaves * 64), 0, st, a); break;
-            case 2: hipLaunchKernelGGL((fewrow_kernel<2>), grid, dim3(kFrWaves * 64), 0, st, a); break;
-            case 4: hipLaunchKernelGGL((fewrow_kernel<4>), grid, dim3(kFrWaves * 64), 0, st, a); break;
-            case 8: hipLaunchKernelGGL((fewrow_kernel<8>), grid, dim3(kFrWaves * 64), 0, st, a); break;
-            default: return PKV_ERR_UNSUPPORTED;
-        }
-        return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    if (fewrow_capable(q_dtype, kv_dtype, head_dim, a.block_size)) {
+        auto fr = [&](auto kvdt) -> int {
+            constexpr int KVDT = decltype(kvdt)::value;
+            switch (group) {
+                case 1: hipLaunchKernelGGL((fewrow_kernel<KVDT, 1>), grid, dim3(kFrWaves * 64), 0, st, a); break;
+                case 2: hipLaunchKernelGGL((fewrow_kernel<KVDT, 2>), grid, dim3(kFrWaves * 64), 0, st, a); break;
+                case 4: hipLaunchKernelGGL((fewrow_kernel<KVDT, 4>), grid, dim3(kFrWaves * 64), 0, st, a); break;
+                case 8: hipLaunchKernelGGL((fewrow_kernel<KVDT, 8>), grid, dim3(kFrWaves * 64), 0, st, a); break;
+                default: return PKV_ERR_UNSUPPORTED;
+            }
+            return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+        };
+        if (kv_dtype == PKV_DTYPE_BF16) return fr(std::integral_constant<int, PKV_DTYPE_BF16>{});
+        return fr(std::integral_constant<int, PKV_DTYPE_FP8_E4M3>{});
     }
     // other caches, head dims and pages: the register-staged prefill tile
     // over the decode queues, one kv head of a unit after the other
