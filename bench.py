@@ -679,12 +679,14 @@ def main():
         roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                              "chunk_tflops": round(mfma_tflops, 2)}
     # the device's measured streaming-read rate for as many bytes as one call
-    # reads, beside the published peak
-    peak_gbs = probe_read_GBps(torch, attn_bytes)
-    roofline["measured_peak"] = {"value": round(peak_gbs, 1), "unit": "GB/s",
-                                 "what": "streaming-read probe (libpkv_probe.so): contiguous, 16 B per lane, "
-                                         "non-temporal, one 8-wave workgroup per CU, as many bytes as one call"}
-    roofline["frac_of_measured_peak"] = round(attn_bytes / call_s / 1e9 / peak_gbs, 4)
+    # reads, beside the published peak (an HBM-bound call only: the probe
+    # measures bytes, not matrix-core flops)
+    if roofline["bound"] == "hbm":
+        peak_gbs = probe_read_GBps(torch, attn_bytes)
+        roofline["measured_peak"] = {"value": round(peak_gbs, 1), "unit": "GB/s",
+                                     "what": "streaming-read probe (libpkv_probe.so): contiguous, 16 B per lane, "
+                                             "non-temporal, one 8-wave workgroup per CU, as many bytes as one call"}
+        roofline["frac_of_measured_peak"] = round(attn_bytes / call_s / 1e9 / peak_gbs, 4)
 
     variant_desc = "".join([f", soft-cap {args.soft_cap:g}" if args.soft_cap else "",
                             f", window {args.window}" if args.window else ""])
