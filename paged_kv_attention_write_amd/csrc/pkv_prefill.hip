@@ -153,6 +153,10 @@ __device__ __forceinline__ void pf_stage(const PfRegs<KVDT, D>& r, const PfRole<
     store_words<4>(&lds.v[buf][role.kk][role.dg * 8], v);
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum; v_maximum3_f32 on
+// gfx950, which needs no quieting of its inputs).
+__device__ __forceinline__ float vmax(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
 __device__ __forceinline__ bf16x8_t lds_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
@@ -340,13 +344,17 @@ __device__ __forceinline__ void pf_update(const Tile& T, float (&sv)[PB][8], int
         // otherwise the pair's maximum is formed across its lanes and the
         // pair rescales.
         const float* s8 = sv[pb];
-        const float ml = fmaxf(fmaxf(fmaxf(s8[0], s8[1]), fmaxf(s8[2], s8[3])),
-                               fmaxf(fmaxf(s8[4], s8[5]), fmaxf(s8[6], s8[7])));
-        const float mtl = (ml == -INFINITY) ? -INFINITY : ml * qk;  // this lane's tile maximum in log2 units
+        // NaN-propagating maxima (v_maximum3_f32) take the products' raw
+        // outputs as they are, where fmaxf would first quiet each of them; a
+        // NaN score comes only from non-finite K or q, whose row is NaN
+        // either way.  qk > 0, so -inf stays -inf when scaled.
+        const float ml =
+            vmax(vmax(vmax(s8[0], s8[1]), vmax(s8[2], s8[3])), vmax(vmax(s8[4], s8[5]), vmax(s8[6], s8[7])));
+        const float mtl = ml * qk;  // this lane's tile maximum in log2 units
         if (__any(mtl > m_run[pb] + 8.0f)) {
-            float mr = fmaxf(ml, __shfl_xor(ml, 16));
-            mr = fmaxf(mr, __shfl_xor(mr, 32));
-            const float mt = (mr == -INFINITY) ? -INFINITY : mr * qk;  // the pair's tile maximum
+            float mr = vmax(ml, __shfl_xor(ml, 16));
+            mr = vmax(mr, __shfl_xor(mr, 32));
+            const float mt = mr * qk;  // the pair's tile maximum
             const bool need = mt > m_run[pb] + 8.0f;
             const float m_new = need ? mt : m_run[pb];
             const float alpha = need ? exp2_fast(m_run[pb] - m_new) : 1.f;
