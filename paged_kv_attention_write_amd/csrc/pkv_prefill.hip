@@ -906,6 +906,12 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     // for where they are issued)
     auto stage = [&](int c, const Regs& r) {
         const int t0 = kb + kPfKeys * c;
+        if (t0 + kPfKeys <= kend) {  // every key of the tile is in the unit (uniform)
+#pragma unroll
+            for (int s16 = 0; s16 < 16; ++s16)
+                *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) = fr_bf16(r.x[s16]);
+            return;
+        }
 #pragma unroll
         for (int s16 = 0; s16 < 16; ++s16) {
             const bool zero = j >= 2 && t0 + 16 * (s16 >> 3) + (s16 & 7) + 8 * (j & 1) >= kend;
