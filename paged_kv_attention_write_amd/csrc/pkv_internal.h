@@ -21,9 +21,14 @@ constexpr int kPrefillQRows = 128;
 // block gets pieces in proportion to its share of the chunks' work.
 constexpr int kPrefillMaxPieces = 8;
 constexpr int kPrefillPieceMin = 512;
-// Prefill queues per decode queue: the prefill kernel runs two 8-wave
-// workgroups per CU when the decode launch runs one.
+// Prefill queues per decode queue: a step of chunks alone runs two prefill
+// workgroups per CU.  A step with decode rows as well runs one: the launch
+// that holds both halves fits one decode and one prefill workgroup on a CU,
+// and with a second prefill workgroup per CU half of the prefill queues
+// would wait for the first to finish (measured: the 63-row + 512-row-chunk
+// step 96.9 -> 84.5 us with one).
 constexpr int kPrefillQueuesPerQueue = 2;
+constexpr int kPrefillQueuesPerQueueMixed = 1;
 
 // A step whose longest chunk has at most this many (row, q head) pairs per
 // kv head (a speculative verify step: a few rows per sequence) is planned as

@@ -150,9 +150,11 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         if (decode_rows(L) > 0) decode_tiles += ceil_div(n - range_start(n - L), kTileTokens);
         else if (L > 1) prefill_flops += pairs_of(n, L, 0, L, 0, n) * flops_per_pair * num_kv_heads;
     }
-    // Decode rows and prefill chunks run as two launches, each balanced on
-    // its own queues.
-    const int32_t prefill_queues = prefill_flops > 0 ? kPrefillQueuesPerQueue * num_queues : 0;
+    // Decode rows and prefill chunks are balanced each on their own queues
+    // (whether they then run in one launch or two).
+    const int32_t prefill_queues =
+        prefill_flops > 0 ? (decode_tiles > 0 ? kPrefillQueuesPerQueueMixed : kPrefillQueuesPerQueue) * num_queues
+                          : 0;
 
     // Prefill units: row blocks x kv heads x key pieces of every chunk.
     std::vector<PrefillPiece> prefill;

@@ -238,7 +238,7 @@ def test_mixed_plan_decode_queues_equal_the_decode_plan():
     p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
     units, qoff, _ = pkv.decode_plan_image(p, image)
     npq = p.num_prefill_queues
-    assert npq == 2 * nq and len(qoff) == nq + npq + 1
+    assert npq == nq and len(qoff) == nq + npq + 1  # one prefill queue per decode queue beside decode rows
     dec = np.nonzero(ql == 1)[0]
     want = split_kv_plan(lens[dec].tolist(), nq, unit_cost=1)
     got = [[(int(dec.tolist().index(u[0])), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]]
