@@ -36,10 +36,16 @@ events around every attention call, which feed ``roofline``) and, unless
 attention calls, replayed after each step's re-plan into a fixed-capacity
 workspace; ``value`` and ``ms_per_step`` come from the replays then (both
 step times are in ``graph``), and layer 0's output of the last replay is
-the one checked against the oracle.  ``roofline`` covers the dominant call (the attention
-call: its kernel and the merge kernel), timed with HIP events around every
-call on its stream; with prefill chunks in the step it reads the chunk's
-flops against the bf16 matrix-core peak when that fraction is the larger.
+the one checked against the oracle.  A decode step over bf16 pages of whole
+16-token tiles calls ``paged_attn_decode_write`` (the new tokens written
+inside the decode launch, one call per layer); other steps, and
+``--separate-write``, call ``paged_kv_write`` and then the attention.
+``roofline`` covers
+the dominant call (the attention call, or the call that writes and attends:
+its kernel and the merge kernel, and the new tokens' bytes when it writes them),
+timed with HIP events around every call on its stream; with prefill chunks in
+the step it reads the chunk's flops against the bf16 matrix-core peak when
+that fraction is the larger.
 ``cpu_baseline`` is the fp64 CPU oracle (write + attention of layer 0) timed
 on this host's cores.
 """
@@ -486,6 +492,9 @@ def main():
     ap.add_argument("--queues", type=int, default=0, help="planner decode queues (0: the library default, one per CU)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (scales the HBM byte counters)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="decode steps call paged_kv_write and then paged_attn_decode instead of "
+                         "paged_attn_decode_write (the new tokens written inside the decode launch)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="time the step only as eager launches (by default the step is also captured once as a "
                          "HIP graph of every layer's write + attention, the plan made for a fixed capacity, and "
@@ -560,6 +569,10 @@ def main():
     scale = float(np.float32(1.0 / np.sqrt(128.0)))
     q_lens = st["q_lens"] if mixed else None
     variant = dict(soft_cap=args.soft_cap, window=args.window)
+    # a decode step over bf16 pages of whole 16-token tiles writes its new
+    # tokens inside the decode launch (one call per layer); other steps, and
+    # --separate-write, call the write, then the attention
+    fused = not args.separate_write and not mixed and kv_dtype == "bf16" and st["block_size"] % 16 == 0
     plan = pkv.Plan(st["context_lens"], q_lens, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
                     num_queues=args.queues, **variant)
     stream = torch.cuda.current_stream(dev)
@@ -585,6 +598,14 @@ def main():
         wait_s.append(plan.last_wait_s)
         for l, layer in enumerate(layers):
             ks, vs = scales[l]
+            if fused:
+                if timed_index is not None:
+                    ev_a[timed_index * args.layers + l].record(stream)
+                pkv.paged_attn_decode_write(layer["out"], layer["q"], layer["k_new"], layer["v_new"], slots,
+                                            layer["kc"], layer["vc"], tables, ctx, scale, plan, ks, vs)
+                if timed_index is not None:
+                    ev_b[timed_index * args.layers + l].record(stream)
+                continue
             pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
             if timed_index is not None:
                 ev_a[timed_index * args.layers + l].record(stream)
@@ -622,6 +643,10 @@ def main():
         def layers_only():
             for l, layer in enumerate(layers):
                 ks, vs = scales[l]
+                if fused:
+                    pkv.paged_attn_decode_write(layer["out"], layer["q"], layer["k_new"], layer["v_new"], slots,
+                                                layer["kc"], layer["vc"], tables, ctx, scale, plan, ks, vs)
+                    continue
                 pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
                 if mixed:
                     pkv.paged_attn_mixed(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, cu, ctx, scale,
@@ -653,7 +678,8 @@ def main():
         wall = time.perf_counter() - g0
         graph_info = {"ms_per_step_graph": round(wall * 1e3 / args.steps, 4),
                       "ms_per_step_eager": round(eager_ms_step, 4),
-                      "captured_per_step": f"{args.layers} x (paged_kv_write + attention call)"}
+                      "captured_per_step": (f"{args.layers} x paged_attn_decode_write" if fused else
+                                            f"{args.layers} x (paged_kv_write + attention call)")}
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e12
     # the roofline's call time: the mean over the timed calls, leaving out
@@ -662,19 +688,23 @@ def main():
     # rocprofv3 averages never contain it)
     kept = decode_ms[decode_ms <= 3.0 * float(np.median(decode_ms))]
     call_s = float(kept.mean()) / 1e3
-    hbm_frac = attn_bytes / call_s / (PEAK_HBM_TBS * 1e12)
+    # the timed call's algorithmic bytes: the attention's, and the new
+    # tokens' when the call writes them
+    call_bytes = attn_bytes + (wr_bytes if fused else 0)
+    hbm_frac = call_bytes / call_s / (PEAK_HBM_TBS * 1e12)
     mfma_tflops = chunk_flops / call_s / 1e12
     mfma_frac = mfma_tflops / PEAK_BF16_TFLOPS
     call_name = ("paged_attn_mixed (mixed kernel + merge kernel, one call)" if mixed else
-                 "paged_attn_decode (decode-unit kernel + merge kernel, one call)")
+                 "paged_attn_decode_write (decode-unit kernel writing the step's tokens + merge kernel, one call)"
+                 if fused else "paged_attn_decode (decode-unit kernel + merge kernel, one call)")
     if mixed and mfma_frac > hbm_frac:
         roofline = {"bound": "mfma", "kernel": call_name, "achieved": round(mfma_tflops, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
                     "flops_per_launch": int(chunk_flops), "traffic": None}
     else:
-        roofline = {"bound": "hbm", "kernel": call_name, "achieved": round(attn_bytes / call_s / 1e9, 2),
+        roofline = {"bound": "hbm", "kernel": call_name, "achieved": round(call_bytes / call_s / 1e9, 2),
                     "peak": PEAK_HBM_TBS * 1e3, "unit": "GB/s", "frac": round(hbm_frac, 4),
-                    "bytes_per_launch": int(attn_bytes), "traffic": None}
+                    "bytes_per_launch": int(call_bytes), "traffic": None}
     if mixed:
         roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                              "chunk_tflops": round(mfma_tflops, 2)}
@@ -682,11 +712,11 @@ def main():
     # reads, beside the published peak (an HBM-bound call only: the probe
     # measures bytes, not matrix-core flops)
     if roofline["bound"] == "hbm":
-        peak_gbs = probe_read_GBps(torch, attn_bytes)
+        peak_gbs = probe_read_GBps(torch, call_bytes)
         roofline["measured_peak"] = {"value": round(peak_gbs, 1), "unit": "GB/s",
                                      "what": "streaming-read probe (libpkv_probe.so): contiguous, 16 B per lane, "
                                              "non-temporal, one 8-wave workgroup per CU, as many bytes as one call"}
-        roofline["frac_of_measured_peak"] = round(attn_bytes / call_s / 1e9 / peak_gbs, 4)
+        roofline["frac_of_measured_peak"] = round(call_bytes / call_s / 1e9 / peak_gbs, 4)
 
     variant_desc = "".join([f", soft-cap {args.soft_cap:g}" if args.soft_cap else "",
                             f", window {args.window}" if args.window else ""])
@@ -705,7 +735,7 @@ def main():
         "data": "synthetic: seeded N(0,1) K/V/Q, seeded lengths and shuffled block tables",
         "config": {
             "workload": f"{args.config}: {cfg['desc']}{variant_desc}; one step = plan + {args.layers} layers x "
-                        f"(write + attention)",
+                        f"(write + attention{', in one call' if fused else ''})",
             "num_seqs": int(B),
             "query_rows": int(T),
             "total_context_tokens": int(st["context_lens"].sum()),
@@ -731,7 +761,7 @@ def main():
     }
     if graph_info is not None:
         result["graph"] = graph_info
-    rec = recorded_traffic(args.config) if not variant_desc else None
+    rec = recorded_traffic(args.config + ("+write" if fused else "")) if not variant_desc else None
     if rec is not None:
         result["roofline"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])
         result["roofline"]["traffic_source"] = rec["profile"]

@@ -353,6 +353,44 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
                      void* stream);
 
 /*
+ * paged_attn_decode_write - a decode step's write and attention in one call:
+ * the same result as paged_kv_write(k_new, v_new, new_dtype,
+ * new_token_stride, slot_mapping, num_seqs, k_cache, v_cache, kv_dtype,
+ * num_blocks, block_size, num_kv_heads, head_dim, k_scale, v_scale, stream)
+ * followed by paged_attn_decode(...) with the other arguments, where token s
+ * of k_new / v_new is the new key and value of sequence s: slot_mapping[s]
+ * is the slot of its key context_lens[s] - 1, or < 0 (nothing written for
+ * it).  ("nanoserve", "One engine step", step 3: each layer writes this
+ * step's K/V, then attends; "How to design an LLM serving system",
+ * "PagedAttention": slot_mapping names each new token's slot.)
+ *
+ * With BF16 q, tokens and cache, pages of a multiple of 16 tokens and k_new,
+ * v_new and their token stride 16-byte aligned, the decode launch writes the
+ * tokens itself:
+ * the workgroup whose keys end at a sequence's key context_lens[s] - 1
+ * stores that token before reading any key.  Then a sequence whose
+ * slot_mapping entry is >= 0 but not that key's slot (or whose length
+ * differs from the plan's) gets a NaN row and nothing is written for it; no
+ * other sequence of the batch may read these slots (a page shared by two
+ * sequences is never the one that receives a new token).  Otherwise (other
+ * dtypes, conversions, other pages) the write kernel runs first, then the
+ * decode call, exactly as the two calls.
+ *
+ *   k_new, v_new       device, new_dtype (F32 or BF16), [num_seqs][num_kv_heads][head_dim]
+ *   slot_mapping       device int32 [num_seqs]
+ *   other arguments    as paged_attn_decode (k_cache, v_cache writable here)
+ * Errors: those of paged_kv_write and of paged_attn_decode, every one of
+ * them checked before anything is launched.
+ */
+int paged_attn_decode_write(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_new,
+                            const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                            const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t kv_dtype,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                            const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_attn_decode_noalloc - paged_attn_decode for callers that cannot
  * allocate device memory (code being captured into a HIP graph, serving loops
  * that must not allocate, harnesses that forbid it): the workspace is the

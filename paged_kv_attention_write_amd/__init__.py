@@ -22,6 +22,7 @@ from ._abi import (  # noqa: F401
     default_queues,
     lib,
     paged_attn_decode,
+    paged_attn_decode_write,
     paged_attn_mixed,
     paged_attn_decode_csr,
     paged_attn_mixed_csr,

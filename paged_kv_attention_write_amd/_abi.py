@@ -50,6 +50,7 @@ EXPORTS = (
     "paged_attn_decode_csr",
     "paged_attn_mixed_csr",
     "paged_attn_decode_noalloc",
+    "paged_attn_decode_write",
 )
 
 
@@ -126,6 +127,11 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, i64, i32,
                                         f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_decode.restype = ctypes.c_int
+        # decode with the step's write: out, q, q_dtype, q stride, k_new, v_new, new_dtype, new stride,
+        # slot_mapping, then the decode arguments from k_cache on
+        L.paged_attn_decode_write.argtypes = [vp, vp, i32, i64, vp, vp, i32, i64, vp, vp, vp, i32, vp, i32, vp, i32,
+                                              i32, i32, i32, i64, i32, f32, f32, f32, P(PkvPlan), vp, sz, vp]
+        L.paged_attn_decode_write.restype = ctypes.c_int
         L.paged_attn_mixed.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i64,
                                        i32, f32, f32, f32, P(PkvPlan), vp, sz, vp]
         L.paged_attn_mixed.restype = ctypes.c_int
@@ -415,6 +421,36 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                      float(v_scale), ctypes.byref(plan.desc), _ptr(plan.workspace),
                                      plan.workspace.numel(), _stream(stream, q.device))
     _check(st, "paged_attn_decode")
+
+
+def paged_attn_decode_write(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                            scale: float, plan: Plan, k_scale: float = 1.0, v_scale: float = 1.0,
+                            stream=None) -> None:
+    """A decode step's write and attention in one call: ``paged_kv_write(k_new, v_new,
+    slot_mapping, ...)`` then ``paged_attn_decode(...)``, where token ``s`` of ``k_new`` /
+    ``v_new`` ``[B, H_kv, D]`` is sequence ``s``'s new key and value and ``slot_mapping[s]``
+    the slot of its key ``context_lens[s] - 1`` (or < 0: nothing written)."""
+    torch = _torch()
+    nb, bs, hkv, d = _attn_common(q, k_cache, v_cache, block_tables, context_lens, plan)
+    B, hq = q.shape[0], q.shape[1]
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    _inner_contiguous(k_new, hkv * d, "k_new")
+    _inner_contiguous(v_new, hkv * d, "v_new")
+    if k_new.shape[0] != B or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype or \
+            v_new.stride(0) != k_new.stride(0):
+        raise ValueError("k_new and v_new must be [B, H_kv, D] with one dtype and token stride")
+    if slot_mapping.dtype != torch.int32 or slot_mapping.shape[0] != B or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int32 [B]")
+    with torch.cuda.device(q.device):
+        st = lib().paged_attn_decode_write(_ptr(out), _ptr(q), dtype_code(q), q.stride(0) if B else hq * d,
+                                           _ptr(k_new), _ptr(v_new), dtype_code(k_new),
+                                           k_new.stride(0) if B else hkv * d, _ptr(slot_mapping), _ptr(k_cache),
+                                           _ptr(v_cache), dtype_code(k_cache), _ptr(block_tables),
+                                           block_tables.shape[1], _ptr(context_lens), B, hq, hkv, d, nb, bs,
+                                           float(scale), float(k_scale), float(v_scale), ctypes.byref(plan.desc),
+                                           _ptr(plan.workspace), plan.workspace.numel(), _stream(stream, q.device))
+    _check(st, "paged_attn_decode_write")
 
 
 def _csr_check(kv_indptr, kv_indices, B):

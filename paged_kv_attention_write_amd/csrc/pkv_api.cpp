@@ -110,6 +110,10 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     a.queue_off = reinterpret_cast<const int32_t*>(ws + plan->off_queues);
     a.partial_o = reinterpret_cast<float*>(ws + plan->off_partial_o);
     a.partial_lse = reinterpret_cast<float*>(ws + plan->off_partial_lse);
+    a.slot_mapping = nullptr;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.new_stride = 0;
     return a;
 }
 
@@ -133,10 +137,13 @@ const char* paged_attn_strerror(int status) {
 
 int pkv_abi_version(void) { return PKV_ABI_VERSION; }
 
-int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t new_token_stride,
-                   const int32_t* slot_mapping, int64_t num_tokens, void* k_cache, void* v_cache,
-                   int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
-                   int32_t head_dim, float k_scale, float v_scale, void* stream) {
+}  // extern "C"
+
+// Checks of paged_kv_write, also made by the decode call that writes.
+static int check_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                       const int32_t* slot_mapping, int64_t num_tokens, const void* k_cache, const void* v_cache,
+                       int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                       int32_t head_dim, float k_scale, float v_scale) {
     if (!dtype_ok(new_dtype) || !dtype_ok(cache_dtype) || new_dtype == PKV_DTYPE_FP8_E4M3) return PKV_ERR_DTYPE;
     const bool pair = (new_dtype == cache_dtype) || (new_dtype == PKV_DTYPE_F32 && cache_dtype == PKV_DTYPE_BF16) ||
                       cache_dtype == PKV_DTYPE_FP8_E4M3;
@@ -157,6 +164,19 @@ int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int6
         !aligned(v_cache, out_align))
         return PKV_ERR_SHAPE;
     if (num_blocks > INT64_MAX / block_size) return PKV_ERR_SHAPE;
+    return PKV_OK;
+}
+
+extern "C" {
+
+int paged_kv_write(const void* k_new, const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                   const int32_t* slot_mapping, int64_t num_tokens, void* k_cache, void* v_cache,
+                   int32_t cache_dtype, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, float k_scale, float v_scale, void* stream) {
+    const int st = check_write(k_new, v_new, new_dtype, new_token_stride, slot_mapping, num_tokens, k_cache, v_cache,
+                               cache_dtype, num_blocks, block_size, num_kv_heads, head_dim, k_scale, v_scale);
+    if (st != PKV_OK || num_tokens == 0) return st;
+    const int64_t hd = static_cast<int64_t>(num_kv_heads) * head_dim;
     return launch_kv_write(k_new, v_new, new_dtype, new_token_stride, slot_mapping, num_tokens, k_cache, v_cache,
                            cache_dtype, num_blocks * block_size, static_cast<int32_t>(hd), k_scale, v_scale,
                            stream);
@@ -255,7 +275,8 @@ static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_toke
                        int32_t max_blocks_per_seq, const int32_t* kv_indptr, const int32_t* context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
-                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+                       const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream,
+                       const AttnArgs* write = nullptr) {
     int st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
                              max_blocks_per_seq, context_lens, num_seqs, num_seqs, num_q_heads, num_kv_heads,
                              head_dim, num_blocks, block_size, scale, k_scale, v_scale, plan, workspace,
@@ -267,6 +288,15 @@ static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_toke
                            context_lens, num_q_heads, num_kv_heads, num_blocks, block_size, scale, k_scale, v_scale,
                            plan, workspace);
     a.kv_indptr = kv_indptr;
+    if (write != nullptr) {
+        a.slot_mapping = write->slot_mapping;
+        a.k_new = write->k_new;
+        a.v_new = write->v_new;
+        a.new_stride = write->new_stride;
+        st = launch_decode_write(a, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+        if (st != PKV_OK) return st;
+        return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
+    }
     const int group = num_q_heads / num_kv_heads;
     // fp8 caches: the few-row kernel (products on the matrix cores, the
     // widening done once as a tile is staged) instead of the vector decode
@@ -292,6 +322,54 @@ int paged_attn_decode(void* out, const void* q, int32_t q_dtype, int64_t q_token
     return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
                        nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                        scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
+}
+
+int paged_attn_decode_write(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride, const void* k_new,
+                            const void* v_new, int32_t new_dtype, int64_t new_token_stride,
+                            const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t kv_dtype,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int64_t num_blocks, int32_t block_size, float scale, float k_scale, float v_scale,
+                            const pkv_plan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+    if (block_tables == nullptr && num_seqs > 0) return PKV_ERR_NULL;
+    // every check of both calls before anything is launched
+    int st = check_write(k_new, v_new, new_dtype, new_token_stride, slot_mapping, num_seqs, k_cache, v_cache,
+                         kv_dtype, num_blocks, block_size, num_kv_heads, head_dim, k_scale, v_scale);
+    if (st != PKV_OK) return st;
+    st = check_attention(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                         max_blocks_per_seq, context_lens, num_seqs, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                         num_blocks, block_size, scale, k_scale, v_scale, plan, workspace, workspace_bytes);
+    if (st != PKV_OK) return st;
+    if (plan->max_q_len > 1) return PKV_ERR_PLAN;
+    if (num_seqs == 0) return PKV_OK;
+    // one launch for bf16 tokens into a bf16 cache on pages of whole tiles
+    // (copied as they are, in 16-byte pieces); otherwise the write kernel and
+    // then the decode call
+    const size_t eb = static_cast<size_t>(dt_bytes(kv_dtype));
+    // (the kernel's eight waves take equal numbers of kv heads, and a thread
+    // holds at most two 16-byte pieces of a token)
+    const bool heads_even = 8 % num_kv_heads == 0 || num_kv_heads % 8 == 0;
+    const bool one = q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_BF16 && new_dtype == PKV_DTYPE_BF16 &&
+                     block_size % kTileTokens == 0 && heads_even && num_kv_heads * head_dim <= 4096 &&
+                     aligned(k_new, 16) && aligned(v_new, 16) &&
+                     (static_cast<size_t>(new_token_stride) * eb) % 16 == 0 &&
+                     (static_cast<size_t>(num_kv_heads) * static_cast<size_t>(head_dim) * eb) % 16 == 0;
+    if (!one) {
+        st = paged_kv_write(k_new, v_new, new_dtype, new_token_stride, slot_mapping, num_seqs, k_cache, v_cache,
+                            kv_dtype, num_blocks, block_size, num_kv_heads, head_dim, k_scale, v_scale, stream);
+        if (st != PKV_OK) return st;
+        return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables,
+                           max_blocks_per_seq, nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           num_blocks, block_size, scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream);
+    }
+    AttnArgs w{};
+    w.slot_mapping = slot_mapping;
+    w.k_new = k_new;
+    w.v_new = v_new;
+    w.new_stride = new_token_stride;
+    return decode_impl(out, q, q_dtype, q_token_stride, k_cache, v_cache, kv_dtype, block_tables, max_blocks_per_seq,
+                       nullptr, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                       scale, k_scale, v_scale, plan, workspace, workspace_bytes, stream, &w);
 }
 
 int paged_attn_decode_noalloc(void* out, const void* q, int32_t q_dtype, int64_t q_token_stride,

@@ -33,6 +33,13 @@ struct AttnArgs {
     const int32_t* queue_off;
     float* partial_o;             // [rows][hq][D]
     float* partial_lse;           // [rows][hq], log2 units
+    // A decode step's new tokens written by the decode launch itself (null:
+    // no write): row s of k_new / v_new ([B][hkv][D], the cache's dtype,
+    // token stride new_stride elements) into slot slot_mapping[s].
+    const int32_t* slot_mapping;
+    const void* k_new;
+    const void* v_new;
+    int64_t new_stride;
 };
 
 // A score s in log2 units under the logit soft-cap c (log2 units too):
@@ -114,6 +121,9 @@ __device__ __forceinline__ void store_out(char* dst, const float (&o)[EPL]) {
 
 int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream);
+// The decode kernel that also writes the step's new tokens (bf16 q and K/V,
+// pages of whole 16-token tiles; a.slot_mapping set).
+int launch_decode_write(const AttnArgs& a, int head_dim, int group, int num_queues, void* stream);
 // Prefill chunks: the prefill queues queue0 .. queue0 + num_queues - 1 of
 // the plan; max_q_len (the plan's longest chunk) picks the tile width.
 bool prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group);

@@ -8,7 +8,7 @@
 namespace pkv {
 namespace {
 
-template <int QDT, int KVDT, int D, int G, int NW, int PK, int WPE>
+template <int QDT, int KVDT, int D, int G, int NW, int PK, int WPE, bool WR = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void decode_kernel(AttnArgs a) {
     __shared__ DecodeLds<D, G, NW> lds;
@@ -18,7 +18,7 @@ void decode_kernel(AttnArgs a) {
     const int u_end = qoff[blockIdx.x + 1];
     for (int ui = u_begin; ui < u_end; ++ui) {
         const Unit un = load_unit(units, ui);
-        decode_unit<QDT, KVDT, D, G, NW, PK>(a, un, lds);
+        decode_unit<QDT, KVDT, D, G, NW, PK, WR>(a, un, lds);
     }
 }
 
@@ -352,6 +352,36 @@ int launch_decode(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, in
         return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_BF16>(a, head_dim, group, num_queues, pk, st);
     if (q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_FP8_E4M3)
         return launch_decode_d<PKV_DTYPE_BF16, PKV_DTYPE_FP8_E4M3>(a, head_dim, group, num_queues, pk, st);
+    return PKV_ERR_UNSUPPORTED;
+}
+
+// The decode kernel that also writes the step's new tokens (a.slot_mapping):
+// bf16 q and K/V on pages of whole 16-token tiles, the shape the serving
+// step uses; a separate build so that the plain decode kernel carries none
+// of it.
+int launch_decode_write(const AttnArgs& a, int head_dim, int group, int num_queues, void* stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (a.block_size % kTileTokens != 0 || a.slot_mapping == nullptr) return PKV_ERR_UNSUPPORTED;
+    constexpr int BF = PKV_DTYPE_BF16;
+    auto go = [&](auto d, auto g) {
+        constexpr int D = decltype(d)::value, G = decltype(g)::value;
+        hipLaunchKernelGGL((decode_kernel<BF, BF, D, G, 8, kPageTile, 2, true>), dim3(num_queues), dim3(8 * 64), 0,
+                           st, a);
+        return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    };
+    using D64 = std::integral_constant<int, 64>;
+    using D128 = std::integral_constant<int, 128>;
+    auto by_group = [&](auto d) {
+        switch (group) {
+            case 1: return go(d, std::integral_constant<int, 1>{});
+            case 2: return go(d, std::integral_constant<int, 2>{});
+            case 4: return go(d, std::integral_constant<int, 4>{});
+            case 8: return go(d, std::integral_constant<int, 8>{});
+            default: return static_cast<int>(PKV_ERR_UNSUPPORTED);
+        }
+    };
+    if (head_dim == 64) return by_group(D64{});
+    if (head_dim == 128) return by_group(D128{});
     return PKV_ERR_UNSUPPORTED;
 }
 

@@ -213,12 +213,18 @@ __device__ __forceinline__ void lane_pages(int32_t (&lp)[U], const AttnArgs& a, 
 //     entry's base address is scalar and the lane adds a 32-bit offset;
 //   kPageOne: the lane's page is its row's entry; the slot is the page;
 //   kPageAny: the lane's own table entries (lp) and 64-bit slots.
-template <int KVDT, int D, int U, int KW, int PK, bool FULL>
+// WR (whole-tile pages): key tnew, the step's new token that this launch
+// writes, is read from knew / vnew (the lane's piece of the caller's row)
+// instead of the pool, and so is a masked lane's clamp token (key ke - 1)
+// when it is that key; the tile holding tnew always takes the masked form.
+template <int KVDT, int D, int U, int KW, int PK, bool FULL, bool WR = false>
 __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], const AttnArgs& a,
                                           const int32_t (&pages)[(kTileEntries<U, PK>)], const int32_t (&lp)[U],
                                           const char* kc, const char* vc, int t0, int ke, int row, uint32_t lane_off,
                                           uint32_t head_off, int64_t tok_bytes, int64_t clamp_off, int tbl_n,
-                                          bool& bad) {
+                                          bool& bad, const char* knew = nullptr, const char* vnew = nullptr,
+                                          int tnew = -1) {
+    static_assert(!WR || PK == kPageTile, "the new token is read in place on whole-tile pages");
     const int bs = a.block_size;
     // block ids are int32: a pool of more than 2^31 - 1 blocks is addressed up to that many
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
@@ -249,8 +255,16 @@ __device__ __forceinline__ void load_tile(Words<KW> (&k)[U], Words<KW> (&v)[U], 
                 } else {
                     const bool ok = pok && t0 + 4 * u + row < ke;
                     const int64_t off = ok ? slot0 * tok_bytes + 4 * uu * tok_bytes + lane_off : clamp_off;
-                    k[u] = load_words_nt<KW>(kc + off);
-                    v[u] = load_words_nt<KW>(vc + off);
+                    const char* kp = kc + off;
+                    const char* vp = vc + off;
+                    if constexpr (WR) {
+                        if ((ok ? t0 + 4 * u + row : ke - 1) == tnew) {
+                            kp = knew;
+                            vp = vnew;
+                        }
+                    }
+                    k[u] = load_words_nt<KW>(kp);
+                    v[u] = load_words_nt<KW>(vp);
                 }
             }
         }
@@ -441,6 +455,10 @@ struct DecodeRun {
     // the unit
     Unit un;
     int n, kb, ke, lo, h;  // lo: first key the row sees (its window)
+    // the step's new token, read from the caller's row (tnew < 0: none)
+    const char* knew_lane;
+    const char* vnew_lane;
+    int tnew;
     bool stale;            // the device's lengths or row offsets differ from the plan's
     SeqTable tbl;
     uint32_t head_off, lane_off;
@@ -494,10 +512,21 @@ struct DecodeRun {
         m_run = -INFINITY;  // running max of this lane's head (the head's lanes agree)
         l_run = 0.f;        // running sum of 2^(s - m_run) of this lane's head
         bad = false;
+        tnew = -1;
+    }
+
+    // Key n - 1 of the open unit (this step's new token, which the launch
+    // writes) is read from the caller's k_new / v_new row.
+    __device__ __forceinline__ void take_new_token(const AttnArgs& a) {
+        const int64_t src = static_cast<int64_t>(un.row0) * a.new_stride * KVB;
+        knew_lane = static_cast<const char*>(a.k_new) + src + head_off;
+        vnew_lane = static_cast<const char*>(a.v_new) + src + head_off;
+        tnew = n - 1;
     }
 
     // Keys [ta, tb) of the open unit (tb <= ke).  Tokens past tb are masked:
     // they may belong to another workgroup's range.
+    template <bool WR = false>
     __device__ __forceinline__ void tiles(const AttnArgs& a, int ta, int tb) {
         const char* __restrict__ kc = static_cast<const char*>(a.k_cache);
         const char* __restrict__ vc = static_cast<const char*>(a.v_cache);
@@ -516,12 +545,13 @@ struct DecodeRun {
         for (int t0 = ta + sub * TT; t0 < tb; t0 += step) {
             Words<KW> kr[U], vr[U];
             if constexpr (PK == kPageAny) lane_pages<U>(lp, a, tbl, t0, tb, ke, row);
-            if (t0 + TT <= tb) {
+            if (t0 + TT <= tb && !(WR && tnew >= 0 && t0 + TT > tnew)) {
                 load_tile<KVDT, D, U, KW, PK, true>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off, head_off,
                                                     tok_bytes, clamp_off, tbl.n, bad);
             } else {
-                load_tile<KVDT, D, U, KW, PK, false>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off, head_off,
-                                                     tok_bytes, clamp_off, tbl.n, bad);
+                load_tile<KVDT, D, U, KW, PK, false, WR>(kr, vr, a, pages, lp, kc, vc, t0, tb, row, lane_off,
+                                                         head_off, tok_bytes, clamp_off, tbl.n, bad, knew_lane,
+                                                         vnew_lane, tnew);
             }
             if constexpr (UNIFORM_PAGE) {
                 if (t0 + step < tb) tile_pages<U, PK>(pages, a, tbl, t0 + step, tb);
@@ -641,16 +671,84 @@ struct DecodeRun {
 // at key 0: under a sliding window it starts at its first visible tile.)
 __device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.prow < 0; }
 
+// A decode step's new token (key n - 1 of the unit's sequence, every kv
+// head, K and V) written into the pool by the workgroup whose unit holds that
+// key ("nanoserve", "One engine step": each layer writes this step's K/V,
+// then attends).  That unit reads the key from the caller's row rather than
+// from the pool, and no other workgroup of the launch reads it, so the
+// stores need no ordering against any load of the launch: `load` checks the
+// slot as the unit starts, `store` copies the token's 16-byte pieces (at
+// most two per thread) once the unit is done.  A
+// slot_mapping entry < 0 writes nothing (the key is read from the pool as it
+// is); an entry other than the key's slot, a key on a page outside the pool
+// or a stale plan writes nothing either and marks the row wrong (reported
+// NaN).
+template <int KVDT, int D, int NW>
+struct TokenWrite {
+    static constexpr int KVB = dt_bytes(KVDT);
+    int64_t slot;
+    bool go, wrong;
+
+    __device__ __forceinline__ void load(const AttnArgs& a, const Unit& un) {
+        const int n = un.pos0 + 1;
+        slot = as_const(a.slot_mapping)[un.row0];
+        const SeqTable tbl = seq_table(a, un.seq);
+        const int pidx = page_of(a, n - 1);
+        const int32_t page = tbl.clamped(pidx);
+        const bool in_pool = pidx < tbl.n && page >= 0 && page < a.num_blocks;
+        const int64_t key_slot = static_cast<int64_t>(page) * a.block_size + row_in_page(a, n - 1, pidx);
+        wrong = slot >= 0 && (!in_pool || slot != key_slot || unit_is_stale(a, un));
+        go = slot >= 0 && !wrong;
+    }
+
+    __device__ __forceinline__ void store(const AttnArgs& a, const Unit& un) const {
+        if (!go) return;
+        const int chunks = a.hkv * D * KVB / 16;  // 16-byte pieces of one token's K (or V)
+        const int64_t src_row = static_cast<int64_t>(un.row0) * a.new_stride * KVB;
+        const int64_t row_bytes = static_cast<int64_t>(a.hkv) * D * KVB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = static_cast<int>(threadIdx.x) + i * NW * 64;
+            if (c < 2 * chunks) {
+                const bool v = c >= chunks;
+                const int64_t piece = static_cast<int64_t>(v ? c - chunks : c) * 16;
+                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const char*>(v ? a.v_new : a.k_new) +
+                                                                src_row + piece);
+                char* const dst = const_cast<char*>(static_cast<const char*>(v ? a.v_cache : a.k_cache));
+                *reinterpret_cast<uint4*>(dst + slot * row_bytes + piece) = w;
+            }
+        }
+    }
+};
+
 // One decode unit, all of it, on the calling workgroup: every kv head, whole
-// units to the output row, pieces to their partial row.
-template <int QDT, int KVDT, int D, int G, int NW, int PK>
+// units to the output row, pieces to their partial row.  WR: the unit that
+// holds its sequence's last key also writes the step's new token, reading
+// that key from the caller's row.
+template <int QDT, int KVDT, int D, int G, int NW, int PK, bool WR = false>
 __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, DecodeLds<D, G, NW>& lds) {
     DecodeRun<QDT, KVDT, D, G, NW, PK> run(a);
     const bool direct = unit_is_whole(un);
-    for (int h = run.head0; h < a.hkv; h += run.hstep) {
-        run.open(a, un, h);
-        run.tiles(a, run.kb, run.ke);
-        run.flush(a, lds, direct, un.prow);
+    if constexpr (WR) {
+        const bool writes = un.kv_end == un.pos0 + 1;
+        TokenWrite<KVDT, D, NW> tw;
+        tw.wrong = false;
+        tw.go = false;
+        if (writes) tw.load(a, un);
+        for (int h = run.head0; h < a.hkv; h += run.hstep) {
+            run.open(a, un, h);
+            run.stale |= tw.wrong;
+            if (tw.go) run.take_new_token(a);
+            run.template tiles<true>(a, run.kb, run.ke);
+            run.flush(a, lds, direct, un.prow);
+        }
+        tw.store(a, un);
+    } else {
+        for (int h = run.head0; h < a.hkv; h += run.hstep) {
+            run.open(a, un, h);
+            run.tiles(a, run.kb, run.ke);
+            run.flush(a, lds, direct, un.prow);
+        }
     }
 }
 
