@@ -364,17 +364,17 @@ int paged_attn_mixed(void* out, const void* q, int32_t q_dtype, int64_t q_token_
  * step's K/V, then attends; "How to design an LLM serving system",
  * "PagedAttention": slot_mapping names each new token's slot.)
  *
- * With BF16 q, tokens and cache, pages of a multiple of 16 tokens and k_new,
- * v_new and their token stride 16-byte aligned, the decode launch writes the
- * tokens itself:
- * the workgroup whose keys end at a sequence's key context_lens[s] - 1
- * stores that token before reading any key.  Then a sequence whose
- * slot_mapping entry is >= 0 but not that key's slot (or whose length
- * differs from the plan's) gets a NaN row and nothing is written for it; no
- * other sequence of the batch may read these slots (a page shared by two
- * sequences is never the one that receives a new token).  Otherwise (other
- * dtypes, conversions, other pages) the write kernel runs first, then the
- * decode call, exactly as the two calls.
+ * With BF16 q, tokens and cache, pages of a multiple of 16 tokens,
+ * num_kv_heads * head_dim <= 4096 and k_new, v_new and their token stride
+ * 16-byte aligned, the decode launch writes the tokens itself:
+ * the workgroup whose keys end at a sequence's key context_lens[s] - 1 reads
+ * that key from k_new / v_new rather than from the pool, and copies the
+ * token into its slot once done.  Then a sequence whose slot_mapping entry
+ * is >= 0 but not that key's slot (or whose length differs from the plan's)
+ * gets a NaN row and nothing is written for it; no other sequence of the
+ * batch may read these slots (a page shared by two sequences is never the
+ * one that receives a new token).  Otherwise the write kernel runs first,
+ * then the decode call, exactly as the two calls.
  *
  *   k_new, v_new       device, new_dtype (F32 or BF16), [num_seqs][num_kv_heads][head_dim]
  *   slot_mapping       device int32 [num_seqs]

@@ -346,11 +346,9 @@ int paged_attn_decode_write(void* out, const void* q, int32_t q_dtype, int64_t q
     // (copied as they are, in 16-byte pieces); otherwise the write kernel and
     // then the decode call
     const size_t eb = static_cast<size_t>(dt_bytes(kv_dtype));
-    // (the kernel's eight waves take equal numbers of kv heads, and a thread
-    // holds at most two 16-byte pieces of a token)
-    const bool heads_even = 8 % num_kv_heads == 0 || num_kv_heads % 8 == 0;
+    // (a thread of the 512 copies at most two 16-byte pieces of a token)
     const bool one = q_dtype == PKV_DTYPE_BF16 && kv_dtype == PKV_DTYPE_BF16 && new_dtype == PKV_DTYPE_BF16 &&
-                     block_size % kTileTokens == 0 && heads_even && num_kv_heads * head_dim <= 4096 &&
+                     block_size % kTileTokens == 0 && num_kv_heads * head_dim <= 4096 &&
                      aligned(k_new, 16) && aligned(v_new, 16) &&
                      (static_cast<size_t>(new_token_stride) * eb) % 16 == 0 &&
                      (static_cast<size_t>(num_kv_heads) * static_cast<size_t>(head_dim) * eb) % 16 == 0;

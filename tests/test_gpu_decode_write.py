@@ -58,7 +58,7 @@ def test_fused_write_matches_the_two_calls(gpu, num_queues):
 
 
 @pytest.mark.parametrize("bs", [1, 3, 16, 48])
-@pytest.mark.parametrize("hq,hkv,d", [(16, 4, 128), (8, 8, 64), (8, 1, 128)])
+@pytest.mark.parametrize("hq,hkv,d", [(16, 4, 128), (8, 8, 64), (8, 1, 128), (12, 3, 64), (128, 16, 128)])
 def test_fused_write_shapes(gpu, bs, hq, hkv, d):
     """Pages of whole 16-token tiles (16, 48: one launch) and others (1, 3: the
     write kernel, then the decode call), head shapes, default queues and
