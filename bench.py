@@ -34,9 +34,9 @@ its wall time, in TB/s.  The step is timed twice: as eager launches (with HIP
 events around every attention call, which feed ``roofline``) and, unless
 ``--no-graph``, as one captured HIP graph of all the layers' writes and
 attention calls, replayed after each step's re-plan into a fixed-capacity
-workspace; ``value`` and ``ms_per_step`` come from the replays then (both
-step times are in ``graph``), and layer 0's output of the last replay is
-the one checked against the oracle.  A decode step over bf16 pages of whole
+workspace; ``value`` and ``ms_per_step`` come from the faster of the two
+forms then (both step times, and which one was used, are in ``graph``), and
+layer 0's output of the last replay is the one checked against the oracle.  A decode step over bf16 pages of whole
 16-token tiles calls ``paged_attn_decode_write`` (the new tokens written
 inside the decode launch, one call per layer); other steps, and
 ``--separate-write``, call ``paged_kv_write`` and then the attention.
@@ -680,6 +680,12 @@ def main():
                       "ms_per_step_eager": round(eager_ms_step, 4),
                       "captured_per_step": (f"{args.layers} x paged_attn_decode_write" if fused else
                                             f"{args.layers} x (paged_kv_write + attention call)")}
+    # the step's time: the faster of its two complete forms (eager launches,
+    # or the captured graph replayed after each re-plan); which one is named
+    # in graph.value_from
+    if graph_info is not None:
+        graph_info["value_from"] = "graph" if wall * 1e3 / args.steps <= eager_ms_step else "eager"
+        wall = min(wall, eager_ms_step * args.steps / 1e3)
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e12
     # the roofline's call time: the mean over the timed calls, leaving out

@@ -676,10 +676,10 @@ __device__ __forceinline__ bool unit_is_whole(const Unit& u) { return u.prow < 0
 // key ("nanoserve", "One engine step": each layer writes this step's K/V,
 // then attends).  That unit reads the key from the caller's row rather than
 // from the pool, and no other workgroup of the launch reads it, so the
-// stores need no ordering against any load of the launch: `load` checks the
-// slot as the unit starts, `store` copies the token's 16-byte pieces (at
-// most two per thread) once the unit is done.  A
-// slot_mapping entry < 0 writes nothing (the key is read from the pool as it
+// stores need no ordering against any load of the launch: as the unit starts,
+// `load` checks the slot and `fetch` reads the token's 16-byte pieces (at
+// most two per thread) into registers, so that they have arrived when
+// `store` writes them once the unit is done.  A slot_mapping entry < 0 writes nothing (the key is read from the pool as it
 // is); an entry other than the key's slot, a key on a page outside the pool
 // or a stale plan writes nothing either and marks the row wrong (reported
 // NaN).
@@ -701,10 +701,27 @@ struct TokenWrite {
         go = slot >= 0 && !wrong;
     }
 
-    __device__ __forceinline__ void store(const AttnArgs& a, const Unit& un) const {
-        if (!go) return;
+    uint4 w[2];
+
+    __device__ __forceinline__ void fetch(const AttnArgs& a, const Unit& un) {
         const int chunks = a.hkv * D * KVB / 16;  // 16-byte pieces of one token's K (or V)
         const int64_t src_row = static_cast<int64_t>(un.row0) * a.new_stride * KVB;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int c = static_cast<int>(threadIdx.x) + i * NW * 64;
+            w[i] = uint4{0u, 0u, 0u, 0u};
+            if (c < 2 * chunks) {
+                const bool v = c >= chunks;
+                const int64_t piece = static_cast<int64_t>(v ? c - chunks : c) * 16;
+                w[i] = *reinterpret_cast<const uint4*>(static_cast<const char*>(v ? a.v_new : a.k_new) + src_row +
+                                                       piece);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(const AttnArgs& a, const Unit& un) const {
+        if (!go) return;
+        const int chunks = a.hkv * D * KVB / 16;
         const int64_t row_bytes = static_cast<int64_t>(a.hkv) * D * KVB;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -712,10 +729,8 @@ struct TokenWrite {
             if (c < 2 * chunks) {
                 const bool v = c >= chunks;
                 const int64_t piece = static_cast<int64_t>(v ? c - chunks : c) * 16;
-                const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const char*>(v ? a.v_new : a.k_new) +
-                                                                src_row + piece);
                 char* const dst = const_cast<char*>(static_cast<const char*>(v ? a.v_cache : a.k_cache));
-                *reinterpret_cast<uint4*>(dst + slot * row_bytes + piece) = w;
+                *reinterpret_cast<uint4*>(dst + slot * row_bytes + piece) = w[i];
             }
         }
     }
@@ -734,7 +749,10 @@ __device__ __forceinline__ void decode_unit(const AttnArgs& a, const Unit& un, D
         TokenWrite<KVDT, D, NW> tw;
         tw.wrong = false;
         tw.go = false;
-        if (writes) tw.load(a, un);
+        if (writes) {
+            tw.load(a, un);
+            tw.fetch(a, un);
+        }
         for (int h = run.head0; h < a.hkv; h += run.hstep) {
             run.open(a, un, h);
             run.stale |= tw.wrong;
