@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 /* Status codes. */
 #define PKV_OK 0
@@ -105,7 +105,8 @@ typedef struct pkv_plan {
     int32_t num_partial_rows; /* rows of partial results in the workspace */
     int32_t target_tiles;     /* ideal work per queue, in 16-token tiles */
     int32_t max_q_len;
-    int32_t num_prefill_queues; /* workgroups of the prefill launch (0: no chunk rows) */
+    int32_t num_prefill_queues; /* workgroups of the prefill launch (0: no chunk rows); with
+                                   num_tail_queues, the last of them are tails */
     int32_t num_prefill_units;  /* of num_units; they sit after the decode units */
     int32_t num_wide_merges;  /* merge records listed first: one row each whose pieces are
                                  many (merged by several waves per q head) */
@@ -119,6 +120,9 @@ typedef struct pkv_plan {
     int32_t window_left;      /* sliding window: a row at position p sees keys p - window_left < j <= p
                                  (0: every key up to p) */
     float logits_soft_cap;    /* scores pass through c * tanh(s / c) before the softmax (0: off) */
+    int32_t num_tail_queues;  /* a step with decode rows and chunks: one per decode queue, the
+                                 last prefill queues; in the one-launch mixed step decode
+                                 workgroup q runs tail q after its decode units (0: none) */
     int64_t off_units;        /* byte offsets inside the workspace */
     int64_t off_queues;
     int64_t off_merges;
@@ -128,7 +132,7 @@ typedef struct pkv_plan {
     int64_t workspace_bytes;  /* bytes of workspace the plan uses */
 } pkv_plan;
 
-#define PKV_PLAN_MAGIC 0x504b5634 /* "PKV4" */
+#define PKV_PLAN_MAGIC 0x504b5635 /* "PKV5" */
 
 /* Text of a status code; never NULL. */
 const char* paged_attn_strerror(int status);

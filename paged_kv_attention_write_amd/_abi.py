@@ -32,7 +32,7 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 
-PLAN_MAGIC = 0x504B5634  # "PKV4", PKV_PLAN_MAGIC in include/pkv.h
+PLAN_MAGIC = 0x504B5635  # "PKV5", PKV_PLAN_MAGIC in include/pkv.h
 
 # Symbols include/pkv.h declares (checked by the CPU tests).
 EXPORTS = (
@@ -76,6 +76,7 @@ class PkvPlan(ctypes.Structure):
         ("max_block_merges", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("logits_soft_cap", ctypes.c_float),
+        ("num_tail_queues", ctypes.c_int32),
         ("off_units", ctypes.c_int64),
         ("off_queues", ctypes.c_int64),
         ("off_merges", ctypes.c_int64),

@@ -58,6 +58,8 @@ int check_attention(void* out, const void* q, int32_t q_dtype, int64_t q_token_s
         plan->num_wide_merges + plan->num_block_merges > plan->num_merges ||
         plan->num_wide_merges > plan->max_row_merges || plan->num_block_merges > plan->max_block_merges ||
         plan->num_merges - plan->num_block_merges > plan->max_row_merges || plan->window_left < 0 ||
+        plan->num_tail_queues < 0 || plan->num_tail_queues > plan->num_prefill_queues ||
+        (plan->num_tail_queues != 0 && plan->num_tail_queues != plan->num_queues) ||
         !(plan->logits_soft_cap >= 0.f) || !std::isfinite(plan->logits_soft_cap))
         return PKV_ERR_PLAN;
     if (rows == 0) return PKV_OK;
@@ -455,11 +457,14 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }
-    // decode rows and chunks side by side in one launch; chunks alone take
-    // the prefill kernel, whose wide form needs no room for a decode
-    // workgroup on the CU
+    // decode rows and chunks side by side in one launch, each decode
+    // workgroup then running its tail queue; chunks alone take the prefill
+    // kernel, whose wide form needs no room for a decode workgroup on the CU.
+    // In two launches the tails are prefill workgroups like the others.
     if (chunks && decode_rows && mixed_one_launch(q_dtype, kv_dtype, head_dim, group, block_size)) {
-        st = launch_mixed(a, head_dim, group, plan->num_queues, plan->num_prefill_queues, stream);
+        const int main_queues = plan->num_prefill_queues - plan->num_tail_queues;
+        st = launch_mixed(a, head_dim, group, plan->num_queues, main_queues,
+                          plan->num_tail_queues > 0 ? plan->num_queues + main_queues : -1, stream);
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }

@@ -138,10 +138,13 @@ bool fewrow_capable(int q_dtype, int kv_dtype, int head_dim, int block_size);
 int launch_fewrow(const AttnArgs& a, int q_dtype, int kv_dtype, int head_dim, int group, int num_queues,
                   void* stream);
 // Decode rows and chunks of a mixed step in one launch (bf16 K/V on pages of
-// whole tiles, groups 2 and 4, where one workgroup of each fits a CU).
+// whole tiles, groups 2 and 4, where one workgroup of each fits a CU):
+// num_prefill_queues prefill workgroups beside the decode ones, and decode
+// workgroup q then runs prefill queue tail_queue0 + q (tail_queue0 < 0: no
+// tails).
 bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int block_size);
 int launch_mixed(const AttnArgs& a, int head_dim, int group, int num_decode_queues, int num_prefill_queues,
-                 void* stream);
+                 int tail_queue0, void* stream);
 // max_rows: the most rows of any merge record (1 for a decode-only plan).
 int launch_merge(const AttnArgs& a, const pkv_plan* plan, const void* workspace, int max_rows, int q_dtype,
                  int head_dim, void* stream);

@@ -29,6 +29,14 @@ constexpr int kPrefillPieceMin = 512;
 // step 96.9 -> 84.5 us with one).
 constexpr int kPrefillQueuesPerQueue = 2;
 constexpr int kPrefillQueuesPerQueueMixed = 1;
+// Beside those, a step with decode rows and chunks gives each decode queue a
+// tail queue of prefill pieces, run by the decode workgroup once its decode
+// units are done.  The tails are sized by the time a decode queue's work
+// takes, counted in prefill flops: this many per byte of its K/V tiles (one
+// launch of the 63-row + 512-row-chunk step on MI355X: decode workgroups
+// ended at about 49 us of 18 tiles each, prefill workgroups sharing their CUs
+// at about 64 us of 75.5 MFLOP each).
+constexpr int64_t kMixedFlopsPerDecodeByte = 42;
 
 // A step whose longest chunk has at most this many (row, q head) pairs per
 // kv head (a speculative verify step: a few rows per sequence) is planned as

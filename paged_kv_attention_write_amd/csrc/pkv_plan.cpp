@@ -14,12 +14,16 @@
 // for, the share is raised to cover it and the requests are placed again.
 //
 // Query chunks (more than one new row) are split into blocks of rows, one
-// unit per (row block, kv head, key piece), and run as a launch of their own
-// over a second set of queues: the key range of a row block is cut into as
-// many pieces as its share of the chunks' work is of those queues, so that
-// the units fill them about once; a unit's cost is its matrix-core flops,
-// and the units are placed largest first, each whole on the least-loaded
-// prefill queue.
+// unit per (row block, kv head, key piece), and run over a second set of
+// queues: the key range of a row block is cut into as many pieces as its
+// share of the chunks' work is of those queues, so that the units fill them
+// about once; a unit's cost is its matrix-core flops, and the units are
+// placed largest first, each whole on the least-loaded prefill queue.  In a
+// step with decode rows as well, every decode queue also gets a tail queue
+// of prefill pieces, sized by the time its decode work takes, which its
+// workgroup runs after its decode units; the row blocks are then cut by
+// flops into pieces that fill a prefill queue and pieces about a tail's
+// size.
 //
 // With a sliding window of W keys a row at position p sees keys
 // p - W < j <= p only: the ranges above then start at the first tile that
@@ -45,6 +49,12 @@ struct QueueHeap {
         std::vector<Item> init;
         init.reserve(n);
         for (int32_t i = 0; i < n; ++i) init.emplace_back(0, i);
+        heap = decltype(heap)(std::greater<Item>(), std::move(init));
+    }
+    explicit QueueHeap(const std::vector<int64_t>& loads) {
+        std::vector<Item> init;
+        init.reserve(loads.size());
+        for (size_t i = 0; i < loads.size(); ++i) init.emplace_back(loads[i], static_cast<int32_t>(i));
         heap = decltype(heap)(std::greater<Item>(), std::move(init));
     }
     Item pop() {
@@ -156,71 +166,11 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         prefill_flops > 0 ? (decode_tiles > 0 ? kPrefillQueuesPerQueueMixed : kPrefillQueuesPerQueue) * num_queues
                           : 0;
 
-    // Prefill units: row blocks x kv heads x key pieces of every chunk.
-    std::vector<PrefillPiece> prefill;
     // merge records with their kind: 0 wide (one decode row, many pieces),
     // 1 a block of chunk rows (whatever its row count: a chunk's last block
     // may hold a single row), 2 the other decode rows
     std::vector<std::pair<int32_t, Merge>> merges;
     int64_t partial_rows = 0;
-    for (int32_t s = 0; s < num_seqs; ++s) {
-        const int32_t n = ctx[s];
-        const int32_t L = q_lens ? q_lens[s] : 1;
-        if (L <= 1 || decode_rows(L) > 0) continue;
-        for (int32_t r0 = 0; r0 < L; r0 += block_rows) {
-            const int32_t r1 = std::min(L, r0 + block_rows);
-            const int32_t nr = r1 - r0;
-            const int32_t extent = n - L + r1;  // keys the last row of the block sees
-            const int64_t start = range_start(n - L + r0);  // the first row's first tile
-            const int64_t span = extent - start;
-            // pieces per kv head: the row block's share of the prefill queues
-            // (its work over the chunks' total, rounded to the nearest
-            // count), so that the chunk units fill the prefill queues about
-            // once; at least one, at most kPrefillMaxPieces, none shorter than
-            // kPrefillPieceMin keys.  A row block that fills under half a
-            // unit's pairs (a few speculative rows, say) costs little to cut,
-            // having few partial rows, so it is cut 3x finer and the
-            // least-loaded placement packs the pieces evenly.
-            const int64_t block_flops = pairs_of(n, L, r0, r1, start, extent) * flops_per_pair * num_kv_heads;
-            const int64_t fine = static_cast<int64_t>(nr) * group * 2 < kPrefillQRows ? 3 : 1;
-            const int64_t share = static_cast<int64_t>(std::llround(
-                static_cast<double>(fine * prefill_queues) * static_cast<double>(block_flops) /
-                (static_cast<double>(prefill_flops) * num_kv_heads)));
-            const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, span / kPrefillPieceMin));
-            const int64_t ask = std::min<int64_t>(most, std::max<int64_t>(1, share));
-            const int64_t piece = ceil_div(ceil_div(span, ask), kTileTokens) * kTileTokens;
-            const int32_t parts = static_cast<int32_t>(ceil_div(span, piece));  // no empty piece
-            const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
-            if (parts > 1) {
-                merges.emplace_back(1, Merge{row0[s] + r0, nr, prow0, parts});
-                partial_rows += static_cast<int64_t>(parts) * nr;
-            }
-            for (int32_t c = 0; c < parts; ++c) {
-                const int64_t kb = start + c * piece;
-                const int64_t ke = std::min<int64_t>(extent, kb + piece);
-                const int64_t cost = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
-                for (int32_t h = 0; h < num_kv_heads; ++h) {
-                    const Unit u{s, static_cast<int32_t>(kb), static_cast<int32_t>(ke), row0[s] + r0, nr,
-                                 n - L + r0, parts > 1 ? prow0 + c * nr : -1, kUnitPrefill + h};
-                    prefill.push_back(PrefillPiece{u, cost});
-                }
-            }
-        }
-    }
-
-    // Prefill units, largest first, each whole on the least-loaded prefill queue.
-    std::vector<std::vector<Unit>> pqueues(static_cast<size_t>(prefill_queues));
-    if (prefill_queues > 0) {
-        QueueHeap pheap(prefill_queues);
-        std::stable_sort(prefill.begin(), prefill.end(), [](const PrefillPiece& a, const PrefillPiece& b) {
-            return a.cost > b.cost;
-        });
-        for (const auto& p : prefill) {
-            auto [load, q] = pheap.pop();
-            pqueues[q].push_back(p.unit);
-            pheap.push(load + p.cost, q);
-        }
-    }
 
     // Decode requests, longest first, cut to fill the lightest queue.
     std::vector<int32_t> order;
@@ -292,6 +242,164 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
                           ceil_div(decode_tiles + static_cast<int64_t>(kDecodeUnitCost) * units, num_queues));
     }
 
+    // A step with decode rows and chunks: each decode queue's workgroup, once
+    // its decode units are done, runs a tail queue of prefill pieces.  In
+    // prefill flops, a decode queue's work counts kMixedFlopsPerDecodeByte per
+    // byte of its tiles' K and V (bf16) and every prefill piece one decode
+    // tile of set-up; T is the load at which the prefill queues (one piece of
+    // T - set-up each) and the tails (T - decode work - set-up, when that is
+    // positive) hold all the prefill work.  The chunk row blocks are then cut
+    // into pieces of T - set-up and a remainder in pieces of about a tail's
+    // size, and every piece is placed, largest first, on the least-loaded of
+    // the prefill and tail queues (a tail starting at its decode work).
+    const int32_t tail_queues = decode_tiles > 0 && prefill_flops > 0 ? num_queues : 0;
+    const int64_t tile_flops = kMixedFlopsPerDecodeByte * 2LL * 2LL * kTileTokens * num_kv_heads * head_dim;
+    std::vector<int64_t> tail_load0(static_cast<size_t>(tail_queues), 0);
+    double main_cap = 0.0, tail_cap = 0.0;  // flops of a prefill queue's piece and of a typical tail piece
+    if (tail_queues > 0) {
+        for (int32_t q = 0; q < num_queues; ++q) {
+            int64_t tiles = 0;
+            for (const Unit& u : queues[q]) tiles += ceil_div(u.kv_end - u.kv_begin, kTileTokens) + kDecodeUnitCost;
+            tail_load0[q] = tiles * tile_flops;
+        }
+        const double setup = static_cast<double>(tile_flops);
+        auto held = [&](double T) {
+            double h = static_cast<double>(prefill_queues) * (T - setup);
+            for (int64_t e : tail_load0) h += std::max(0.0, T - static_cast<double>(e) - setup);
+            return h;
+        };
+        double lo = setup, hi = setup + static_cast<double>(prefill_flops) / prefill_queues;
+        for (int it = 0; it < 64; ++it) {
+            const double mid = 0.5 * (lo + hi);
+            (held(mid) < static_cast<double>(prefill_flops) ? lo : hi) = mid;
+        }
+        const double T = hi;
+        main_cap = T - setup;
+        int32_t open = 0;
+        double room = 0.0;
+        for (int64_t e : tail_load0) {
+            const double r = T - static_cast<double>(e) - setup;
+            if (r > 0.0) {
+                room += r;
+                ++open;
+            }
+        }
+        tail_cap = open > 0 ? room / open : 0.0;
+    }
+
+    // Prefill units: row blocks x kv heads x key pieces of every chunk.
+    std::vector<PrefillPiece> prefill;
+    for (int32_t s = 0; s < num_seqs; ++s) {
+        const int32_t n = ctx[s];
+        const int32_t L = q_lens ? q_lens[s] : 1;
+        if (L <= 1 || decode_rows(L) > 0) continue;
+        for (int32_t r0 = 0; r0 < L; r0 += block_rows) {
+            const int32_t r1 = std::min(L, r0 + block_rows);
+            const int32_t nr = r1 - r0;
+            const int32_t extent = n - L + r1;  // keys the last row of the block sees
+            const int64_t start = range_start(n - L + r0);  // the first row's first tile
+            const int64_t span = extent - start;
+            // pieces per kv head: the row block's share of the prefill queues
+            // (its work over the chunks' total, rounded to the nearest
+            // count), so that the chunk units fill the prefill queues about
+            // once; at least one, at most kPrefillMaxPieces, none shorter than
+            // kPrefillPieceMin keys.  A row block that fills under half a
+            // unit's pairs (a few speculative rows, say) costs little to cut,
+            // having few partial rows, so it is cut 3x finer and the
+            // least-loaded placement packs the pieces evenly.
+            const int64_t block_flops = pairs_of(n, L, r0, r1, start, extent) * flops_per_pair * num_kv_heads;
+            const int64_t fine = static_cast<int64_t>(nr) * group * 2 < kPrefillQRows ? 3 : 1;
+            const int64_t share = static_cast<int64_t>(std::llround(
+                static_cast<double>(fine * prefill_queues) * static_cast<double>(block_flops) /
+                (static_cast<double>(prefill_flops) * num_kv_heads)));
+            const int64_t most = std::min<int64_t>(kPrefillMaxPieces, std::max<int64_t>(1, span / kPrefillPieceMin));
+            const int64_t ask = std::min<int64_t>(most, std::max<int64_t>(1, share));
+            const int64_t piece = ceil_div(ceil_div(span, ask), kTileTokens) * kTileTokens;
+            // piece boundaries: key starts of the pieces and the extent
+            std::vector<int64_t> cuts;
+            for (int64_t kb = start; kb < extent; kb += piece) cuts.push_back(kb);
+            cuts.push_back(extent);
+            if (tail_queues > 0 && main_cap > 0.0) {
+                // with tails: pieces of main_cap flops (the remainder of a
+                // block spread over them when it is under half a tail piece),
+                // then the remainder in pieces of about tail_cap (at most
+                // kPrefillMaxPieces in all); each cut on the first 16-key tile
+                // boundary that reaches its share
+                const double u = static_cast<double>(block_flops) / num_kv_heads;
+                // (at most `most` of them, as without tails)
+                int64_t m = std::min<int64_t>(static_cast<int64_t>(u / main_cap), most);
+                double r = u - static_cast<double>(m) * main_cap;
+                int64_t k = 0;
+                if (m == 0) {
+                    k = 1;
+                } else if (r < 0.5 * tail_cap || tail_cap <= 0.0) {
+                    r = 0.0;
+                } else {
+                    k = std::max<int64_t>(1, std::llround(r / tail_cap));
+                }
+                k = std::min<int64_t>(k, std::max<int64_t>(kPrefillMaxPieces - m, 1));
+                m = std::min<int64_t>(m, kPrefillMaxPieces - k);
+                std::vector<double> at;  // cumulative flops at each inner cut
+                const double mainc = m > 0 ? (u - r) / static_cast<double>(m) : 0.0;
+                for (int64_t c = 1; c <= m; ++c) at.push_back(mainc * static_cast<double>(c));
+                for (int64_t c = 1; c < k; ++c) at.push_back(u - r + r * static_cast<double>(c) / static_cast<double>(k));
+                if (!at.empty() && at.back() >= u - 0.5) at.pop_back();  // no empty last piece
+                cuts.assign(1, start);
+                const int64_t tiles = ceil_div(span, kTileTokens);
+                for (double want : at) {
+                    // the smallest tile count whose keys reach `want` flops
+                    int64_t lo = 1, hi = tiles;
+                    while (lo < hi) {
+                        const int64_t mid = (lo + hi) / 2;
+                        const double got = static_cast<double>(
+                            pairs_of(n, L, r0, r1, start, std::min<int64_t>(extent, start + mid * kTileTokens)) *
+                            flops_per_pair);
+                        if (got >= want) hi = mid;
+                        else lo = mid + 1;
+                    }
+                    const int64_t kb = std::min<int64_t>(extent, start + lo * kTileTokens);
+                    if (kb > cuts.back() && kb < extent) cuts.push_back(kb);
+                }
+                cuts.push_back(extent);
+            }
+            const int32_t parts = static_cast<int32_t>(cuts.size()) - 1;
+            const int32_t prow0 = parts > 1 ? static_cast<int32_t>(partial_rows) : -1;
+            if (parts > 1) {
+                merges.emplace_back(1, Merge{row0[s] + r0, nr, prow0, parts});
+                partial_rows += static_cast<int64_t>(parts) * nr;
+            }
+            for (int32_t c = 0; c < parts; ++c) {
+                const int64_t kb = cuts[c];
+                const int64_t ke = cuts[c + 1];
+                const int64_t cost = pairs_of(n, L, r0, r1, kb, ke) * flops_per_pair;
+                for (int32_t h = 0; h < num_kv_heads; ++h) {
+                    const Unit u{s, static_cast<int32_t>(kb), static_cast<int32_t>(ke), row0[s] + r0, nr,
+                                 n - L + r0, parts > 1 ? prow0 + c * nr : -1, kUnitPrefill + h};
+                    prefill.push_back(PrefillPiece{u, cost});
+                }
+            }
+        }
+    }
+
+    // Prefill units, largest first, each whole on the least-loaded prefill queue.
+    // With tails: over the prefill queues, then the tails (queue
+    // prefill_queues + q: decode queue q's), each piece adding its set-up.
+    std::vector<std::vector<Unit>> pqueues(static_cast<size_t>(prefill_queues + tail_queues));
+    if (prefill_queues > 0) {
+        std::vector<int64_t> load0(static_cast<size_t>(prefill_queues + tail_queues), 0);
+        for (int32_t q = 0; q < tail_queues; ++q) load0[prefill_queues + q] = tail_load0[q];
+        QueueHeap pheap(load0);
+        const int64_t setup = tail_queues > 0 ? tile_flops : 0;
+        std::stable_sort(prefill.begin(), prefill.end(), [](const PrefillPiece& a, const PrefillPiece& b) {
+            return a.cost > b.cost;
+        });
+        for (const auto& p : prefill) {
+            auto [load, q] = pheap.pop();
+            pqueues[q].push_back(p.unit);
+            pheap.push(load + p.cost + setup, q);
+        }
+    }
+
     // merge records: wide ones, then row blocks, then the other one-row
     // records, each kind in its order
     std::stable_sort(merges.begin(), merges.end(),
@@ -317,8 +425,9 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     if (num_units > INT32_MAX || partial_rows > INT32_MAX) return PKV_ERR_SHAPE;
 
     // Image: [units][queue offsets][merges], then the partial results.  The
-    // decode queues' units come first, then the prefill queues'; the queue
-    // offsets run over both (num_queues + prefill_queues + 1 entries).
+    // decode queues' units come first, then the prefill queues', then the
+    // tails'; the queue offsets run over all of them (num_queues +
+    // prefill_queues + tail_queues + 1 entries, at most 3 num_queues + 1).
     // Section sizes: the plan's own, or those of the capacity (the same
     // offsets for every plan of that capacity, queues and heads).
     PlanSections sec{num_units, plan_counts_index(num_queues) + kPlanCounts, static_cast<int64_t>(merges.size()),
@@ -348,7 +457,8 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
     plan->num_partial_rows = static_cast<int32_t>(partial_rows);
     plan->target_tiles = static_cast<int32_t>(std::min<int64_t>(target, INT32_MAX));
     plan->max_q_len = max_q;
-    plan->num_prefill_queues = prefill_queues;
+    plan->num_prefill_queues = prefill_queues + tail_queues;
+    plan->num_tail_queues = tail_queues;
     plan->num_prefill_units = static_cast<int32_t>(num_prefill_units);
     plan->num_wide_merges = num_wide;
     plan->num_block_merges = num_block;
@@ -378,11 +488,11 @@ int plan_host(const int32_t* ctx, const int32_t* q_lens, int32_t num_seqs, int32
         qoff[q] = cursor;
         for (const Unit& x : queues[q]) u[cursor++] = x;
     }
-    for (int32_t q = 0; q < prefill_queues; ++q) {
+    for (int32_t q = 0; q < prefill_queues + tail_queues; ++q) {
         qoff[num_queues + q] = cursor;
         for (const Unit& x : pqueues[q]) u[cursor++] = x;
     }
-    qoff[num_queues + prefill_queues] = cursor;
+    qoff[num_queues + prefill_queues + tail_queues] = cursor;
     int32_t* counts = qoff + plan_counts_index(num_queues);
     counts[0] = static_cast<int32_t>(merges.size());
     counts[1] = num_wide;

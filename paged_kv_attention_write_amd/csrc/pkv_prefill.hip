@@ -977,22 +977,32 @@ __device__ __forceinline__ void mixed_decode_queue(const AttnArgs& a, int b, Dec
 
 template <int KVDT, int D, int G, bool RING>
 __global__ __launch_bounds__(kPfWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-void mixed_kernel(AttnArgs a, int num_decode_queues) {
+void mixed_kernel(AttnArgs a, int num_decode_queues, int tail_queue0) {
     static_assert(KVDT == PKV_DTYPE_BF16, "one launch for bf16 K/V");
     const int b = blockIdx.x;
+    // a decode workgroup's tail: prefill queue tail_queue0 + b, once every
+    // wave is done with the decode units' LDS
     if constexpr (RING) {
         __shared__ __attribute__((aligned(16))) uint16_t s0[ring_stage0_elems<D, G>()], s1[kRingStageElems],
             s2[kRingStageElems], s3[kRingStageElems];
-        if (b < num_decode_queues)
+        if (b < num_decode_queues) {
             mixed_decode_queue<D, G>(a, b, *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(s0));
-        else
+            if (tail_queue0 < 0) return;
+            __syncthreads();
+            prefill_queue_ring<G, kPfWaves>(a, tail_queue0 + b, s0, s1, s2, s3);
+        } else {
             prefill_queue_ring<G, kPfWaves>(a, b, s0, s1, s2, s3);
+        }
     } else {
         __shared__ __attribute__((aligned(16))) char smem[mixed_lds_bytes<KVDT, D, G>()];
-        if (b < num_decode_queues)
+        if (b < num_decode_queues) {
             mixed_decode_queue<D, G>(a, b, *reinterpret_cast<DecodeLds<D, G, kPfWaves>*>(smem));
-        else
+            if (tail_queue0 < 0) return;
+            __syncthreads();
+            prefill_queue<KVDT, D, G>(a, tail_queue0 + b, *reinterpret_cast<PrefillLds<D>*>(smem));
+        } else {
             prefill_queue<KVDT, D, G>(a, b, *reinterpret_cast<PrefillLds<D>*>(smem));
+        }
     }
 }
 
@@ -1047,21 +1057,27 @@ int launch_prefill_d(const AttnArgs& a, int d, int group, int max_pairs, int num
 
 template <int KVDT>
 int launch_mixed_d(const AttnArgs& a, int d, int group, int num_decode_queues, int num_prefill_queues,
-                   hipStream_t st) {
+                   int tail_queue0, hipStream_t st) {
     const dim3 grid(num_decode_queues + num_prefill_queues), block(kPfWaves * 64);
     const bool ring = ring_pages(a);
     if (d == 128 && group == 4 && ring)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, true>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, true>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else if (d == 128 && group == 4)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, false>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 4, false>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else if (d == 128 && group == 2 && ring)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, true>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, true>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else if (d == 128 && group == 2)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, false>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 128, 2, false>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else if (d == 64 && group == 4)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 4, false>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 4, false>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else if (d == 64 && group == 2)
-        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 2, false>), grid, block, 0, st, a, num_decode_queues);
+        hipLaunchKernelGGL((mixed_kernel<KVDT, 64, 2, false>), grid, block, 0, st, a, num_decode_queues,
+                           tail_queue0);
     else
         return PKV_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
@@ -1121,8 +1137,8 @@ bool mixed_one_launch(int q_dtype, int kv_dtype, int head_dim, int group, int bl
 }
 
 int launch_mixed(const AttnArgs& a, int head_dim, int group, int num_decode_queues, int num_prefill_queues,
-                 void* stream) {
-    return launch_mixed_d<PKV_DTYPE_BF16>(a, head_dim, group, num_decode_queues, num_prefill_queues,
+                 int tail_queue0, void* stream) {
+    return launch_mixed_d<PKV_DTYPE_BF16>(a, head_dim, group, num_decode_queues, num_prefill_queues, tail_queue0,
                                           static_cast<hipStream_t>(stream));
 }
 

@@ -34,7 +34,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(declared) == set(_abi.EXPORTS), declared
     for name in declared:
         assert hasattr(L, name), name
-    assert L.pkv_abi_version() == 5
+    assert L.pkv_abi_version() == 6
 
 
 def test_strerror_covers_all_codes():
@@ -232,13 +232,14 @@ def test_window_shrinks_decode_work():
 
 def test_mixed_plan_decode_queues_equal_the_decode_plan():
     """Decode rows of a mixed step are placed exactly as a decode-only plan of
-    those sequences would place them; chunk units sit on the prefill queues."""
+    those sequences would place them; chunk units sit on the prefill queues:
+    one per decode queue, then a tail queue per decode queue."""
     lens, ql = _mixed_case()
     nq = 96
     p, image = pkv.plan_host(lens, ql, 32, 8, 128, nq)
     units, qoff, _ = pkv.decode_plan_image(p, image)
     npq = p.num_prefill_queues
-    assert npq == nq and len(qoff) == nq + npq + 1  # one prefill queue per decode queue beside decode rows
+    assert p.num_tail_queues == nq and npq == 2 * nq and len(qoff) == nq + npq + 1
     dec = np.nonzero(ql == 1)[0]
     want = split_kv_plan(lens[dec].tolist(), nq, unit_cost=1)
     got = [[(int(dec.tolist().index(u[0])), int(u[1]), int(u[2])) for u in units[qoff[q]:qoff[q + 1]]]
@@ -389,6 +390,39 @@ def test_prefill_units_are_balanced():
     lens = workloads.structure_only("decode", "page16")["context_lens"]
     c = _prefill_queue_costs(lens, np.full(lens.shape[0], 8, np.int32))
     assert c.max() <= 1.1 * c.mean(), c.max() / c.mean()
+
+
+def test_mixed_plan_tails_balance_decode_and_prefill_queues():
+    """A step with decode rows and chunks: each prefill queue holds one piece
+    of the chunk, their flops within 2 % of each other, and each decode
+    queue's tail holds prefill pieces that bring the decode queue's work
+    (its tiles at the planner's rate of 42 prefill flops per byte of K/V, a
+    tile per unit of set-up) plus the tail's flops (and a tile of set-up per
+    piece) to at most 10 % over a prefill queue's."""
+    import workloads
+
+    st = workloads.structure_only("mixed", "page16")
+    lens, ql = st["context_lens"], st["q_lens"]
+    hkv, d, nq = 8, 128, 256
+    p, image = pkv.plan_host(lens, ql, 32, hkv, d, nq)
+    units, qoff, _ = pkv.decode_plan_image(p, image)
+    assert p.num_tail_queues == nq and p.num_prefill_queues == 2 * nq
+    tile = 42 * 2 * 2 * 16 * hkv * d
+    fpp = 4 * (32 // hkv) * d
+
+    def flops(u):
+        seq, kb, ke, row0, nrows, pos0 = (int(x) for x in u[:6])
+        return sum(max(0, min(ke - 1, pos0 + r) - kb + 1) for r in range(nrows)) * fpp + tile
+
+    main = np.array([sum(flops(u) for u in units[qoff[q]:qoff[q + 1]]) for q in range(nq, 2 * nq)], float)
+    assert all(qoff[q + 1] - qoff[q] == 1 for q in range(nq, 2 * nq))
+    assert main.max() <= 1.02 * main.min(), (main.max(), main.min())
+    both = np.array([sum(((int(u[2]) - int(u[1]) + 15) // 16 + 1) * tile for u in units[qoff[q]:qoff[q + 1]]) +
+                     sum(flops(u) for u in units[qoff[2 * nq + q]:qoff[2 * nq + q + 1]]) for q in range(nq)], float)
+    assert both.max() <= 1.1 * main.mean(), both.max() / main.mean()
+    # every tail piece is a chunk unit
+    tails = units[qoff[2 * nq]:qoff[3 * nq]]
+    assert len(tails) > 0 and np.all(tails[:, 7] >= 1)
 
 
 @pytest.mark.parametrize("group,rows", [(4, 4), (1, 16), (8, 2), (2, 8), (4, 3)])
