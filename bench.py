@@ -40,12 +40,16 @@ layer 0's output of the last replay is the one checked against the oracle.  A de
 16-token tiles calls ``paged_attn_decode_write`` (the new tokens written
 inside the decode launch, one call per layer); other steps, and
 ``--separate-write``, call ``paged_kv_write`` and then the attention.
-``roofline`` covers
-the dominant call (the attention call, or the call that writes and attends:
-its kernel and the merge kernel, and the new tokens' bytes when it writes them),
-timed with HIP events around every call on its stream; with prefill chunks in
-the step it reads the chunk's flops against the bf16 matrix-core peak when
-that fraction is the larger.
+``roofline`` covers the dominant kernel: the attention kernel of the
+attention call (or of the call that writes and attends), timed with HIP
+events on its stream from before the call to the event the library records
+between that kernel and the merge kernel (``pkv_set_split_event``, set on
+every other timed step: the record costs its call about 3 us), against the
+call's algorithmic bytes (and the new tokens' when it writes them);
+``roofline.call`` gives the same for the whole call, merge kernel included,
+from the timed steps without the split event.
+With prefill chunks in the step it reads the chunk's flops against the bf16
+matrix-core peak when that fraction is the larger.
 ``cpu_baseline`` is the fp64 CPU oracle (write + attention of layer 0) timed
 on this host's cores.
 """
@@ -589,8 +593,21 @@ def main():
     n_events = args.steps * args.layers
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    # recorded by the library between each timed call's attention kernel and
+    # its merge kernel (pkv_set_split_event); each is recorded once here so
+    # that its HIP event exists
+    ev_m = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+    for e in ev_m:
+        e.record(stream)
+    torch.cuda.synchronize()
     plan_s = []
     wait_s = []
+
+    # the split event costs its call about 3 us (a record between the two
+    # kernels), so with two or more timed steps it is set on the odd ones
+    # only: those give the attention kernel's time, the even ones the call's
+    def split_step(i):
+        return args.steps < 2 or i % 2 == 1
 
     def step(timed_index=None):
         plan.update(st["context_lens"], q_lens)
@@ -598,6 +615,8 @@ def main():
         wait_s.append(plan.last_wait_s)
         for l, layer in enumerate(layers):
             ks, vs = scales[l]
+            if timed_index is not None and split_step(timed_index):
+                pkv.set_split_event(ev_m[timed_index * args.layers + l])
             if fused:
                 if timed_index is not None:
                     ev_a[timed_index * args.layers + l].record(stream)
@@ -605,6 +624,7 @@ def main():
                                             layer["kc"], layer["vc"], tables, ctx, scale, plan, ks, vs)
                 if timed_index is not None:
                     ev_b[timed_index * args.layers + l].record(stream)
+                    pkv.set_split_event(None)
                 continue
             pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
             if timed_index is not None:
@@ -617,6 +637,7 @@ def main():
                                       ks, vs)
             if timed_index is not None:
                 ev_b[timed_index * args.layers + l].record(stream)
+                pkv.set_split_event(None)
 
     log("warmup")
     for _ in range(args.warmup):
@@ -630,7 +651,13 @@ def main():
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    decode_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    pkv.set_split_event(None)
+    split = np.array([split_step(i) for i in range(args.steps) for _ in range(args.layers)])
+    all_call_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    # call times from the steps without the split event (all of them when
+    # there is a single timed step), kernel times from those with it
+    decode_ms = all_call_ms[~split] if np.any(~split) else all_call_ms
+    kernel_ms = np.array([a.elapsed_time(m) for a, m, sp in zip(ev_a, ev_m, split) if sp])
     eager_ms_step = wall * 1e3 / args.steps
     graph_info = None
     if args.graph:
@@ -688,29 +715,49 @@ def main():
         wall = min(wall, eager_ms_step * args.steps / 1e3)
     ms_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e12
-    # the roofline's call time: the mean over the timed calls, leaving out
-    # calls above 3x the median (a host-side gap between the events and the
-    # launch, milliseconds long, once in hundreds of calls; the kernels'
-    # rocprofv3 averages never contain it)
+    # mean over the timed calls, leaving out calls above 3x the median (a
+    # host-side gap between the events and the launch, milliseconds long,
+    # once in hundreds of calls; the kernels' rocprofv3 averages never
+    # contain it)
+    def kept_mean_s(ms):
+        kept_ = ms[ms <= 3.0 * float(np.median(ms))]
+        return float(kept_.mean()) / 1e3, int(ms.size - kept_.size)
+
     kept = decode_ms[decode_ms <= 3.0 * float(np.median(decode_ms))]
-    call_s = float(kept.mean()) / 1e3
-    # the timed call's algorithmic bytes: the attention's, and the new
-    # tokens' when the call writes them
+    call_s, _ = kept_mean_s(decode_ms)
+    # the roofline's kernel: the call's attention kernel, from the event
+    # before the call to the event the library records between that kernel
+    # and the merge kernel
+    kern_s, kern_left_out = kept_mean_s(kernel_ms)
+    # the algorithmic bytes of the call (all read or written by its
+    # attention kernel): the attention's, and the new tokens' when the call
+    # writes them
     call_bytes = attn_bytes + (wr_bytes if fused else 0)
-    hbm_frac = call_bytes / call_s / (PEAK_HBM_TBS * 1e12)
-    mfma_tflops = chunk_flops / call_s / 1e12
+    hbm_frac = call_bytes / kern_s / (PEAK_HBM_TBS * 1e12)
+    mfma_tflops = chunk_flops / kern_s / 1e12
     mfma_frac = mfma_tflops / PEAK_BF16_TFLOPS
-    call_name = ("paged_attn_mixed (mixed kernel + merge kernel, one call)" if mixed else
-                 "paged_attn_decode_write (decode-unit kernel writing the step's tokens + merge kernel, one call)"
-                 if fused else "paged_attn_decode (decode-unit kernel + merge kernel, one call)")
-    if mixed and mfma_frac > hbm_frac:
-        roofline = {"bound": "mfma", "kernel": call_name, "achieved": round(mfma_tflops, 2),
+    kern_name = ("mixed_kernel (the attention kernel of paged_attn_mixed)" if mixed else
+                 "decode_kernel writing the step's tokens (the attention kernel of paged_attn_decode_write)"
+                 if fused else "decode_kernel (the attention kernel of paged_attn_decode)")
+    call_name = ("paged_attn_mixed (mixed kernel + merge kernel)" if mixed else
+                 "paged_attn_decode_write (decode kernel writing the step's tokens + merge kernel)"
+                 if fused else "paged_attn_decode (decode kernel + merge kernel)")
+    mfma_bound = mixed and mfma_frac > hbm_frac
+    if mfma_bound:
+        roofline = {"bound": "mfma", "kernel": kern_name, "achieved": round(mfma_tflops, 2),
                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(mfma_frac, 4),
                     "flops_per_launch": int(chunk_flops), "traffic": None}
     else:
-        roofline = {"bound": "hbm", "kernel": call_name, "achieved": round(call_bytes / call_s / 1e9, 2),
+        roofline = {"bound": "hbm", "kernel": kern_name, "achieved": round(call_bytes / kern_s / 1e9, 2),
                     "peak": PEAK_HBM_TBS * 1e3, "unit": "GB/s", "frac": round(hbm_frac, 4),
                     "bytes_per_launch": int(call_bytes), "traffic": None}
+    roofline["kernel_us"] = round(kern_s * 1e6, 3)
+    roofline["kernel_left_out_above_3x_median"] = kern_left_out
+    # the whole call (its merge kernel and the gap before it included)
+    call_rate = chunk_flops / call_s / 1e12 if mfma_bound else call_bytes / call_s / 1e9
+    call_peak = PEAK_BF16_TFLOPS if mfma_bound else PEAK_HBM_TBS * 1e3
+    roofline["call"] = {"what": call_name, "us": round(call_s * 1e6, 3), "achieved": round(call_rate, 2),
+                        "frac": round(call_rate / call_peak, 4)}
     if mixed:
         roofline["other"] = {"hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
                              "chunk_tflops": round(mfma_tflops, 2)}
@@ -722,7 +769,8 @@ def main():
         roofline["measured_peak"] = {"value": round(peak_gbs, 1), "unit": "GB/s",
                                      "what": "streaming-read probe (libpkv_probe.so): contiguous, 16 B per lane, "
                                              "non-temporal, one 8-wave workgroup per CU, as many bytes as one call"}
-        roofline["frac_of_measured_peak"] = round(call_bytes / call_s / 1e9 / peak_gbs, 4)
+        roofline["frac_of_measured_peak"] = round(call_bytes / kern_s / 1e9 / peak_gbs, 4)
+        roofline["call"]["frac_of_measured_peak"] = round(call_bytes / call_s / 1e9 / peak_gbs, 4)
 
     variant_desc = "".join([f", soft-cap {args.soft_cap:g}" if args.soft_cap else "",
                             f", window {args.window}" if args.window else ""])
@@ -769,7 +817,8 @@ def main():
         result["graph"] = graph_info
     rec = recorded_traffic(args.config + ("+write" if fused else "")) if not variant_desc else None
     if rec is not None:
-        result["roofline"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])
+        result["roofline"]["traffic"] = int(rec["kernel_read_bytes"] + rec["kernel_written_bytes"])
+        result["roofline"]["call"]["traffic"] = int(rec["read_bytes"] + rec["written_bytes"])
         result["roofline"]["traffic_source"] = rec["profile"]
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")

@@ -141,6 +141,20 @@ const char* paged_attn_strerror(int status);
 int pkv_abi_version(void);
 
 /*
+ * pkv_set_split_event - a timing hook (a measurement aid; no page defines
+ * it).  While `event` (a hipEvent_t passed as void*, created by the caller)
+ * is not NULL, every attention call (paged_attn_decode,
+ * paged_attn_decode_write, paged_attn_mixed, their _csr forms and
+ * paged_attn_decode_noalloc) records it on its stream after launching its
+ * attention kernel(s) and before launching its merge kernel, so that the
+ * attention kernel's time can be read beside the whole call's.  The setting
+ * is process-wide and unsynchronised: set it from the thread that makes the
+ * calls, and keep it NULL while a stream is being captured.  A call whose
+ * record fails returns PKV_ERR_HIP.  Returns PKV_OK.
+ */
+int pkv_set_split_event(void* event);
+
+/*
  * paged_kv_write - write this step's K/V rows into the block pool by slot.
  *
  * For every token t with 0 <= slot_mapping[t] < num_blocks * block_size:

@@ -28,5 +28,6 @@ from ._abi import (  # noqa: F401
     paged_attn_mixed_csr,
     paged_kv_write,
     plan_host,
+    set_split_event,
     strerror,
 )

@@ -38,6 +38,7 @@ PLAN_MAGIC = 0x504B5635  # "PKV5", PKV_PLAN_MAGIC in include/pkv.h
 EXPORTS = (
     "paged_attn_strerror",
     "pkv_abi_version",
+    "pkv_set_split_event",
     "paged_kv_write",
     "paged_attn_workspace_size",
     "paged_attn_default_queues",
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_strerror.restype = ctypes.c_char_p
         L.pkv_abi_version.argtypes = []
         L.pkv_abi_version.restype = ctypes.c_int
+        L.pkv_set_split_event.argtypes = [ctypes.c_void_p]
+        L.pkv_set_split_event.restype = ctypes.c_int
         L.paged_kv_write.argtypes = [vp, vp, i32, i64, vp, i64, vp, vp, i32, i64, i32, i32, i32, f32, f32, vp]
         L.paged_kv_write.restype = ctypes.c_int
         L.paged_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, P(sz), P(sz)]
@@ -149,6 +152,19 @@ def lib() -> ctypes.CDLL:
         L.paged_attn_decode_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def set_split_event(event) -> None:
+    """Timing hook (pkv_set_split_event): while ``event`` (a ``torch.cuda.Event``
+    that has been recorded once, or a raw hipEvent_t as an int) is not None,
+    every attention call records it on its stream between its attention
+    kernel and its merge kernel.  Process-wide; keep it None during capture."""
+    handle = None
+    if event is not None:
+        handle = int(event.cuda_event) if hasattr(event, "cuda_event") else int(event)
+        if handle == 0:
+            raise ValueError("set_split_event: the event has no HIP event yet (record it once first)")
+    _check(lib().pkv_set_split_event(handle), "pkv_set_split_event")
 
 
 def strerror(status: int) -> str:

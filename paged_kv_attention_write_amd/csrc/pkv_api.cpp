@@ -119,9 +119,23 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
     return a;
 }
 
+// Timing hook of pkv_set_split_event: recorded on a call's stream between
+// its attention kernel and its merge kernel.
+hipEvent_t g_split_event = nullptr;
+
+int mark_split(void* stream) {
+    if (g_split_event == nullptr) return PKV_OK;
+    return hipEventRecord(g_split_event, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+int pkv_set_split_event(void* event) {
+    g_split_event = static_cast<hipEvent_t>(event);
+    return PKV_OK;
+}
 
 const char* paged_attn_strerror(int status) {
     switch (status) {
@@ -296,6 +310,7 @@ static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_toke
         a.v_new = write->v_new;
         a.new_stride = write->new_stride;
         st = launch_decode_write(a, head_dim, num_q_heads / num_kv_heads, plan->num_queues, stream);
+        if (st == PKV_OK) st = mark_split(stream);
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
     }
@@ -308,6 +323,7 @@ static int decode_impl(void* out, const void* q, int32_t q_dtype, int64_t q_toke
         st = launch_fewrow(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
     else
         st = launch_decode(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
+    if (st == PKV_OK) st = mark_split(stream);
     if (st != PKV_OK) return st;
     return launch_merge(a, plan, workspace, 1, q_dtype, head_dim, stream);
 }
@@ -454,6 +470,7 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
     const bool decode_rows = plan->num_units > plan->num_prefill_units;
     if (few) {
         st = launch_fewrow(a, q_dtype, kv_dtype, head_dim, group, plan->num_queues, stream);
+        if (st == PKV_OK) st = mark_split(stream);
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }
@@ -465,6 +482,7 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
         const int main_queues = plan->num_prefill_queues - plan->num_tail_queues;
         st = launch_mixed(a, head_dim, group, plan->num_queues, main_queues,
                           plan->num_tail_queues > 0 ? plan->num_queues + main_queues : -1, stream);
+        if (st == PKV_OK) st = mark_split(stream);
         if (st != PKV_OK) return st;
         return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
     }
@@ -477,6 +495,8 @@ static int mixed_impl(void* out, const void* q, int32_t q_dtype, int64_t q_token
                             plan->num_queues, stream);
         if (st != PKV_OK) return st;
     }
+    st = mark_split(stream);
+    if (st != PKV_OK) return st;
     return launch_merge(a, plan, workspace, merge_rows(plan, group), q_dtype, head_dim, stream);
 }
 

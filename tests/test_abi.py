@@ -35,6 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in declared:
         assert hasattr(L, name), name
     assert L.pkv_abi_version() == 6
+    assert L.pkv_set_split_event(None) == 0  # the timing hook, off
 
 
 def test_strerror_covers_all_codes():
