@@ -149,8 +149,8 @@ int pkv_abi_version(void);
  * attention kernel(s) and before launching its merge kernel, so that the
  * attention kernel's time can be read beside the whole call's.  The setting
  * is process-wide and unsynchronised: set it from the thread that makes the
- * calls, and keep it NULL while a stream is being captured.  A call whose
- * record fails returns PKV_ERR_HIP.  Returns PKV_OK.
+ * calls, and keep it NULL while a stream is being captured.  A record that
+ * fails is skipped; the call's work is launched either way.  Returns PKV_OK.
  */
 int pkv_set_split_event(void* event);
 

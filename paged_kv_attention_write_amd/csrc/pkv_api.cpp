@@ -120,12 +120,15 @@ AttnArgs make_args(void* out, const void* q, int64_t q_token_stride, const void*
 }
 
 // Timing hook of pkv_set_split_event: recorded on a call's stream between
-// its attention kernel and its merge kernel.
+// its attention kernel and its merge kernel.  A record that fails is skipped
+// (and its error cleared, so that the merge launch's check does not see it):
+// the call's work is launched either way.
 hipEvent_t g_split_event = nullptr;
 
 int mark_split(void* stream) {
-    if (g_split_event == nullptr) return PKV_OK;
-    return hipEventRecord(g_split_event, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+    if (g_split_event != nullptr && hipEventRecord(g_split_event, static_cast<hipStream_t>(stream)) != hipSuccess)
+        (void)hipGetLastError();
+    return PKV_OK;
 }
 
 }  // namespace
