@@ -736,10 +736,13 @@ def main():
     hbm_frac = call_bytes / kern_s / (PEAK_HBM_TBS * 1e12)
     mfma_tflops = chunk_flops / kern_s / 1e12
     mfma_frac = mfma_tflops / PEAK_BF16_TFLOPS
-    kern_name = ("mixed_kernel (the attention kernel of paged_attn_mixed)" if mixed else
+    few_rows = mixed and int(st["q_lens"].max()) * 4 <= 16  # 32 q / 8 kv heads: G = 4
+    decode_rows_in_step = bool(np.any(st["q_lens"] == 1))
+    mixed_kern = ("fewrow_kernel" if few_rows else "mixed_kernel" if decode_rows_in_step else "prefill kernel")
+    kern_name = (f"{mixed_kern} (the attention kernel of paged_attn_mixed)" if mixed else
                  "decode_kernel writing the step's tokens (the attention kernel of paged_attn_decode_write)"
                  if fused else "decode_kernel (the attention kernel of paged_attn_decode)")
-    call_name = ("paged_attn_mixed (mixed kernel + merge kernel)" if mixed else
+    call_name = (f"paged_attn_mixed ({mixed_kern} + merge kernel)" if mixed else
                  "paged_attn_decode_write (decode kernel writing the step's tokens + merge kernel)"
                  if fused else "paged_attn_decode (decode kernel + merge kernel)")
     mfma_bound = mixed and mfma_frac > hbm_frac

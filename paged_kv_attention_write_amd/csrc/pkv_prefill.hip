@@ -817,10 +817,12 @@ void prefill_wide_kernel(AttnArgs a, int queue0) {
 // 32-key tiles on its own, with no barrier: it loads a tile's K and V rows
 // into registers (each load instruction two whole 256-byte rows of K and
 // two of V), writes them to an LDS tile of its own in the ring layout and
-// reads the operands back as the ring path does.  The next tile's loads go
-// out once the current tile is in LDS, before its products: one tile in
-// flight per wave measured faster than two (the read rate of the pool falls
-// with more bytes in flight per CU, as for the decode kernel).  All loads go
+// reads the operands back as the ring path does.  One tile is in flight per
+// wave (two measured slower: the read rate of the pool falls with more bytes
+// in flight per CU, as for the decode kernel): for fp8 codes the next tile's
+// loads go out once the current tile is in LDS, before its products (their
+// widening then overlaps the loads); for bf16 after the products (1 % faster
+// on a speculative verify step).  All loads go
 // to registers, so the compiler's waits for them count exactly.  bf16 K/V,
 // D = 128, pages of a power of two >= 16 tokens (each 16-key half of a tile
 // lies in one page).
@@ -925,8 +927,13 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     issue(0, r);
     for (int c = 0; c < ntiles; ++c) {
         stage(c, r);
-        issue(c + 1, r);
-        W.template tile<D / 32>(a, RingTile{st}, kb + kPfKeys * c);
+        if constexpr (KVDT == PKV_DTYPE_BF16) {
+            W.template tile<D / 32>(a, RingTile{st}, kb + kPfKeys * c);
+            issue(c + 1, r);
+        } else {
+            issue(c + 1, r);
+            W.template tile<D / 32>(a, RingTile{st}, kb + kPfKeys * c);
+        }
     }
     W.close(a, un);
 }
