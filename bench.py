@@ -187,16 +187,21 @@ def cpu_baseline(torch, st, layer, kv_dtype, scales, budget_s=10.0, soft_cap=0.0
 COPY_BYTES = 1 << 30
 
 # Sources that define the kernels of one paged_attn_decode call (decode and
-# merge kernels, the plan they walk).  A traffic record taken from the byte
-# counters is reported only while these sources are unchanged.
+# merge kernels, the plan they walk); a paged_attn_mixed call also runs the
+# prefill, mixed and few-row kernels.  A traffic record taken from the byte
+# counters is reported only while the sources of its call are unchanged.
 DECODE_SOURCES = ["pkv_decode.hip", "pkv_decode_unit.h", "pkv_device.h", "pkv_attention.h", "pkv_internal.h", "pkv_plan.cpp"]
+MIXED_SOURCES = DECODE_SOURCES + ["pkv_prefill.hip"]
+# configs whose calls go through paged_attn_mixed, or through the few-row
+# kernel (fp8 decode)
+PREFILL_CONFIGS = ("mixed", "mixed-chunk", "specverify", "fp8prefix")
 
 
-def decode_source_digest():
+def decode_source_digest(sources=None):
     import hashlib
 
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources or DECODE_SOURCES:
         with open(os.path.join(ROOT, "paged_kv_attention_write_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -209,7 +214,7 @@ def recorded_traffic(config):
     d = os.path.join(ROOT, "profiles")
     if not os.path.isdir(d):
         return None
-    digest = decode_source_digest()
+    digest = decode_source_digest(MIXED_SOURCES if config.split("+")[0] in PREFILL_CONFIGS else DECODE_SOURCES)
     for name in sorted(os.listdir(d)):
         if not name.endswith(".md"):
             continue
