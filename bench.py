@@ -15,13 +15,15 @@ prefill chunk packed in one step; "nanoserve" chunked prefill) and
 ``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
 peak), ``specverify`` (64 sequences with 4 new rows each, a speculative
 verify step, through the mixed path).  ``--study skew``, ``--study
-plan-cost``, ``--study pages`` and ``--study read-peak`` print, instead of
-the bench line, one JSON line per case of the load-balance study (length
-mixes of equal total tokens at batch 4-128), the planner-cost sweep (batch
-8-512), the page-size sweep (pages of 1/4/16/64 tokens and a contiguous slab
-at 64 x 4K, 16 x 16K and 256 x 1K keys, each case's layer 0 checked against
-the oracle on sampled sequences) and the measured read ceilings of the
-streaming-read probe.
+plan-cost``, ``--study pages``, ``--study read-peak`` and ``--study gather``
+print, instead of the bench line, one JSON line per case of the load-balance
+study (length mixes of equal total tokens at batch 4-128), the planner-cost
+sweep (batch 8-512), the page-size sweep (pages of 1/4/16/64 tokens and a
+contiguous slab at 64 x 4K, 16 x 16K and 256 x 1K keys, each case's layer 0
+checked against the oracle on sampled sequences), the measured read ceilings
+of the streaming-read probe, and the decode call against the gather path it
+replaces (K/V gathered into a padded contiguous copy, then dense attention
+in torch; a comparator only, never part of the library).
 
 Inputs are synthetic: block tables, lengths and slots come from the seeded
 generator in workloads/; K/V/Q values are N(0, 1) drawn on the GPU from a
@@ -469,6 +471,75 @@ def pages_cpu_baseline(torch, st, layer, scale, samples=6):
             "parity": {"max_abs_err": err, "bound": bound, "ok": bool(np.all(np.isfinite(got[rows])) and err <= bound)}}
 
 
+def gather_attention(torch, layer, tables, lens, bs, scale, hq=32, hkv=8, d=128):
+    """The gather path the paged kernel replaces: every sequence's pages
+    gathered into a padded contiguous K/V copy ([B, L] keys, L = the table's
+    width in keys), then dense attention by batched products (bf16 operands,
+    each one contiguous; scores and softmax in fp32, keys past a sequence's
+    length masked).  Returns (out [B, hq, d], seconds of the gather, of the
+    products) from HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    B, mb = tables.shape
+    L = mb * bs
+    g = hq // hkv
+    e0.record(stream)
+    idx = tables.clamp(min=0).long()
+    kt = layer["kc"][idx].reshape(B, L, hkv, d).permute(0, 2, 3, 1).contiguous().reshape(B * hkv, d, L)
+    vv = layer["vc"][idx].reshape(B, L, hkv, d).permute(0, 2, 1, 3).contiguous().reshape(B * hkv, L, d)
+    e1.record(stream)
+    q = layer["q"].reshape(B * hkv, g, d).contiguous()
+    s = torch.bmm(q, kt).float() * scale
+    live = (torch.arange(L, device=s.device)[None, :] < lens[:, None]).repeat_interleave(hkv, dim=0)
+    s = s.masked_fill(~live[:, None, :], float("-inf"))
+    p = torch.softmax(s, dim=-1).to(torch.bfloat16).contiguous()
+    out = torch.bmm(p, vv).reshape(B, hq, d)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    return out, e0.elapsed_time(e1) * 1e-3, e1.elapsed_time(e2) * 1e-3
+
+
+def study_gather(args, torch, pkv, workloads, byte_model):
+    """The paged decode call against the gather path it replaces ("nanoserve"
+    reports its Triton paged decode 13.7-18.5x faster than gathering K/V and
+    running dense attention): the decode workload, one layer, p50 of the
+    timed calls of each, and the two outputs compared."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    scale = float(np.float32(1.0 / np.sqrt(128.0)))
+    st = workloads.structure_only("decode", "page16")
+    layer = build_layers(torch, st, {"config": "decode"}, 1, dev)[0]
+    tables = torch.from_numpy(st["block_tables"]).to(dev)
+    ctx = torch.from_numpy(st["context_lens"]).to(dev)
+    plan = pkv.Plan(st["context_lens"], None, num_q_heads=32, num_kv_heads=8, head_dim=128, device=dev,
+                    num_queues=args.queues)
+    paged_ms, gather_s, attn_s = [], [], []
+    for it in range(args.warmup + args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        pkv.paged_attn_decode(layer["out"], layer["q"], layer["kc"], layer["vc"], tables, ctx, scale, plan)
+        b.record(stream)
+        ref, gs, ats = gather_attention(torch, layer, tables, ctx, st["block_size"], scale)
+        if it >= args.warmup:
+            paged_ms.append(a.elapsed_time(b))
+            gather_s.append(gs)
+            attn_s.append(ats)
+    torch.cuda.synchronize()
+    nbytes = byte_model.attention_bytes(st["context_lens"], st["q_lens"], 32, 8, 128, st["block_size"], 2, 2)
+    paged = float(np.median(paged_ms)) * 1e-3
+    gath = float(np.median(np.array(gather_s) + np.array(attn_s)))
+    print(json.dumps({
+        "study": "gather", "workload": "decode: 64 seqs, ctx U[512,4096], 32q/8kv, D=128, page 16, bf16",
+        "paged_call_us": round(paged * 1e6, 2),
+        "gather_path_us": round(gath * 1e6, 2),
+        "gather_us": round(float(np.median(gather_s)) * 1e6, 2),
+        "dense_attention_us": round(float(np.median(attn_s)) * 1e6, 2),
+        "paged_speedup": round(gath / paged, 2),
+        "paged_TBps": round(nbytes / paged / 1e12, 4),
+        "max_abs_diff_paged_vs_gather": float((layer["out"].float() - ref.float()).abs().max()),
+        "calls": len(paged_ms)}), flush=True)
+
+
 def study_plan_cost(args, torch, pkv, workloads):
     """Host planner cost per step (reused by all layers) for batch 8..512 with
     context uniform in [512, 4096], one JSON line per batch."""
@@ -512,11 +583,11 @@ def main():
                     help="attention variant: logit soft-cap c (scores through c * tanh(s / c)); 0: off")
     ap.add_argument("--window", type=int, default=0,
                     help="attention variant: sliding window of W keys (a row at p sees p - W < j <= p); 0: off")
-    ap.add_argument("--study", choices=["skew", "plan-cost", "pages", "read-peak"],
+    ap.add_argument("--study", choices=["skew", "plan-cost", "pages", "read-peak", "gather"],
                     help="instead of the bench line: the load-balance study over length mixes (skew), the "
                          "planner cost over batch sizes (plan-cost), the page-size sweep with its parity check "
-                         "(pages) or the streaming-read ceilings of the read probe (read-peak), one JSON line "
-                         "per case")
+                         "(pages), the streaming-read ceilings of the read probe (read-peak) or the paged decode "
+                         "call against a gather + dense attention path in torch (gather), one JSON line per case")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); sharding across GPUs is not built",
@@ -544,6 +615,9 @@ def main():
         return
     if args.study == "read-peak":
         study_read_peak(args, torch, workloads)
+        return
+    if args.study == "gather":
+        study_gather(args, torch, pkv, workloads, byte_model)
         return
 
     cfg = CONFIGS[args.config]
