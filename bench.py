@@ -679,6 +679,8 @@ def main():
     for e in ev_m:
         e.record(stream)
     torch.cuda.synchronize()
+    # before each separate paged_kv_write call (its time: to ev_a)
+    ev_w = [torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
     plan_s = []
     wait_s = []
 
@@ -705,6 +707,8 @@ def main():
                     ev_b[timed_index * args.layers + l].record(stream)
                     pkv.set_split_event(None)
                 continue
+            if timed_index is not None:
+                ev_w[timed_index * args.layers + l].record(stream)
             pkv.paged_kv_write(layer["k_new"], layer["v_new"], slots, layer["kc"], layer["vc"], ks, vs)
             if timed_index is not None:
                 ev_a[timed_index * args.layers + l].record(stream)
@@ -737,6 +741,14 @@ def main():
     # there is a single timed step), kernel times from those with it
     decode_ms = all_call_ms[~split] if np.any(~split) else all_call_ms
     kernel_ms = np.array([a.elapsed_time(m) for a, m, sp in zip(ev_a, ev_m, split) if sp])
+    # the separate write call (HIP events around it), or a note that the
+    # decode launch writes the tokens
+    if fused:
+        write_us = {"note": "written inside the decode launch (paged_attn_decode_write)"}
+    else:
+        wms = np.array([w.elapsed_time(a) for w, a in zip(ev_w, ev_a)])
+        write_us = {"p50": round(float(np.median(wms)) * 1e3, 3), "mean": round(float(wms.mean()) * 1e3, 3),
+                    "bytes": int(wr_bytes)}
     eager_ms_step = wall * 1e3 / args.steps
     graph_info = None
     if args.graph:
@@ -888,6 +900,7 @@ def main():
                               "max": round(float(decode_ms.max()) * 1e3, 3),
                               "roofline_mean": round(call_s * 1e6, 3),
                               "left_out_above_3x_median": int(decode_ms.size - kept.size)},
+        "write_call_us": write_us,
         "plan_us_per_step": round(float(np.median(plan_s)) * 1e6, 2),
         "plan_us_per_layer": round(float(np.median(plan_s)) * 1e6 / args.layers, 3),
         "plan_staging_wait_us_per_step": round(float(np.median(wait_s)) * 1e6, 2),
