@@ -922,6 +922,10 @@ def main():
         got = layers[0]["out"].float().cpu().numpy().astype(np.float64)
         cb_out = cb.pop("out")
         result["parity_max_abs_layer0"] = float(np.max(np.abs(got - cb_out)))
+        # the oracle's time per layer-call (write + attention) over the GPU's
+        # (the attention call, and the separate write when there is one)
+        gpu_layer_s = call_s + (0.0 if fused else float(write_us["mean"]) * 1e-6)
+        cb["oracle_s_over_gpu_s_per_layer_call"] = round(float(cb["seconds_per_layer_call"]) / gpu_layer_s, 1)
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
