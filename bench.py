@@ -10,7 +10,8 @@ step and reused by every layer, as the planner's description on "How Easy Is
 It to Start Serving LLMs?" (Phase 4 §3) has it.  Other workloads:
 ``long-page1`` / ``long-page16`` / ``long-contig`` (16 x 32768 keys, the
 scattered-vs-contiguous comparison), ``fp8prefix`` (128 sequences over a
-shared 4096-token prefix, fp8 cache), ``mixed`` (63 decodes and one 512-row
+shared 4096-token prefix, fp8 cache; ``bf16prefix`` the same with a bf16
+cache, for the comparison), ``mixed`` (63 decodes and one 512-row
 prefill chunk packed in one step; "nanoserve" chunked prefill) and
 ``mixed-chunk`` (that chunk alone, to read the matrix-core tile against its
 peak), ``specverify`` (64 sequences with 4 new rows each, a speculative
@@ -78,7 +79,11 @@ CONFIGS = {
     "long-page1": dict(config="long", layout="page1", desc="16 seqs x 32768, 32q/8kv, D=128, page 1 shuffled, bf16"),
     "long-page16": dict(config="long", layout="page16", desc="16 seqs x 32768, 32q/8kv, D=128, page 16 shuffled, bf16"),
     "long-contig": dict(config="long", layout="contig", desc="16 seqs x 32768, 32q/8kv, D=128, contiguous slab, bf16"),
-    "fp8prefix": dict(config="fp8prefix", layout="page16", desc="128 seqs, 4096 shared + 256 private tokens, fp8 E4M3 KV"),
+    "fp8prefix": dict(config="fp8prefix", layout="page16", kv="fp8",
+                      desc="128 seqs, 4096 shared + 256 private tokens, fp8 E4M3 KV"),
+    "bf16prefix": dict(config="fp8prefix", layout="page16",
+                       desc="the fp8prefix sequences and shared pages with a bf16 KV cache (the fp8 cache's "
+                            "comparison)"),
     "mixed": dict(config="mixed", layout="page16",
                   desc="63 decodes (ctx U[256,2048]) + one 512-row chunk over 2048 cached tokens, packed T=575, "
                        "32q/8kv, D=128, page 16, bf16"),
@@ -102,7 +107,7 @@ def build_layers(torch, st, cfg, layers, dev):
     hq, hkv, d = 32, 8, 128
     nb, bs = st["num_blocks"], st["block_size"]
     B = int(st["q_lens"].sum())  # query rows (one per sequence for decode)
-    fp8 = cfg["config"] == "fp8prefix"
+    fp8 = cfg.get("kv") == "fp8"
     out = []
     for l in range(layers):
         g = torch.Generator(device=dev)
@@ -638,7 +643,7 @@ def main():
     B = st["context_lens"].shape[0]
     T = int(st["q_lens"].sum())
     mixed = bool(np.any(st["q_lens"] > 1))
-    kv_dtype = "fp8" if cfg["config"] == "fp8prefix" else "bf16"
+    kv_dtype = cfg.get("kv", "bf16")
     kvb = 1 if kv_dtype == "fp8" else 2
     log(f"building {args.layers} layers of {args.config}")
     layers = build_layers(torch, st, cfg, args.layers, dev)
@@ -832,8 +837,10 @@ def main():
     mixed_kern = ("fewrow_kernel" if few_rows else "mixed_kernel" if decode_rows_in_step else "prefill kernel")
     kern_name = (f"{mixed_kern} (the attention kernel of paged_attn_mixed)" if mixed else
                  "decode_kernel writing the step's tokens (the attention kernel of paged_attn_decode_write)"
-                 if fused else "decode_kernel (the attention kernel of paged_attn_decode)")
+                 if fused else "fewrow_kernel (the attention kernel of paged_attn_decode on an fp8 cache)"
+                 if kv_dtype == "fp8" else "decode_kernel (the attention kernel of paged_attn_decode)")
     call_name = (f"paged_attn_mixed ({mixed_kern} + merge kernel)" if mixed else
+                 "paged_attn_decode (few-row kernel + merge kernel)" if kv_dtype == "fp8" and not fused else
                  "paged_attn_decode_write (decode kernel writing the step's tokens + merge kernel)"
                  if fused else "paged_attn_decode (decode kernel + merge kernel)")
     mfma_bound = mixed and mfma_frac > hbm_frac
