@@ -678,6 +678,11 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
         const SeqTable tbl = W.tbl;
         const int ntiles = kend > kb ? (kend - kb + kPfKeys - 1) / kPfKeys : 0;
         const int glast = kend > kb ? ((kend - 1) & ~15) : kb;  // start of the unit's last 16 keys
+        // bytes of a pool row (one key, every kv head) and of a page; this
+        // unit's kv head within a row
+        const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * (D * 2);
+        const uint64_t page_bytes = static_cast<uint64_t>(row_bytes) << shift;
+        const char* const head_src = lane_src + static_cast<uint32_t>(h) * (D * 2);
 
         // a half of 16 keys starting at t0 + 16 f, clamped to the last half
         // (so that a half past kend reads keys that exist), and its
@@ -697,8 +702,9 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
                 const int pidx = g >> shift;
                 const bool ok = pidx < tbl.n && static_cast<uint32_t>(ef) < nblocks;
                 W.bad |= t0 + 16 * f < kend && !ok;
-                const int64_t row0 = static_cast<int64_t>(ok ? ef : 0) * a.block_size + (g - (pidx << shift));
-                const char* const src = lane_src + (row0 * a.hkv + h) * (D * 2);
+                const uint64_t in_page = static_cast<uint64_t>(static_cast<uint32_t>(g - (pidx << shift))) * row_bytes;
+                const char* const src = head_src + static_cast<uint64_t>(static_cast<uint32_t>(ok ? ef : 0)) * page_bytes +
+                                        in_page;
 #pragma unroll
                 for (int e = 0; e < SE; ++e)
                     __builtin_amdgcn_global_load_lds(src + e * slot_src_step,
