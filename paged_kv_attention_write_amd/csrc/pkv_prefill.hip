@@ -869,10 +869,12 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     const uint32_t nblocks = static_cast<uint32_t>(a.num_blocks < 0x7FFFFFFF ? a.num_blocks : 0x7FFFFFFF);
     const int shift = a.block_shift;
     const uint32_t row_bytes = static_cast<uint32_t>(a.hkv) * RB;  // pool row of one key
+    const uint64_t page_bytes = static_cast<uint64_t>(row_bytes) << a.block_shift;
     // this lane's source in slot i of a half: key i + 8 (j % 2) of the half,
     // K (j < 2) or V, logical chunk (lane % 16) ^ (j % 2)
     const char* const src = static_cast<const char*>(j < 2 ? a.k_cache : a.v_cache) + (8 * (j & 1)) * row_bytes +
                             static_cast<uint32_t>(((lane & 15) ^ (j & 1)) * PIECE);
+    const char* const head_src = src + static_cast<uint32_t>(h) * RB;  // this kv head within a pool row
 
     // the unit's pairs as "wave 0" of a layout of one pair block per wave
     PfWave<D, G, kPfWaves, 1> W;
@@ -899,8 +901,19 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
             const int32_t e = tbl.clamped(pidx);
             const bool ok = pidx < tbl.n && static_cast<uint32_t>(e) < nblocks;
             W.bad |= t0 + 16 * f < kend && !ok;
-            const int64_t row0 = live ? static_cast<int64_t>(ok ? e : 0) * a.block_size + (g - (pidx << shift)) : 0;
-            const char* const base = src + (row0 * a.hkv + h) * RB;
+            // fp8 codes: the page id times the page's bytes plus the row's
+            // offset (fewer scalar instructions: measured faster there, not
+            // for bf16)
+            const char* base;
+            if constexpr (KVDT == PKV_DTYPE_FP8_E4M3) {
+                base = live ? head_src + static_cast<uint64_t>(static_cast<uint32_t>(ok ? e : 0)) * page_bytes +
+                                  static_cast<uint64_t>(static_cast<uint32_t>(g - (pidx << shift))) * row_bytes
+                            : head_src;
+            } else {
+                const int64_t row0 =
+                    live ? static_cast<int64_t>(ok ? e : 0) * a.block_size + (g - (pidx << shift)) : 0;
+                base = src + (row0 * a.hkv + h) * RB;
+            }
 #pragma unroll
             for (int i8 = 0; i8 < 8; ++i8)
                 r.x[8 * f + i8] = __builtin_nontemporal_load(
