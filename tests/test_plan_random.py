@@ -151,6 +151,13 @@ def test_random_batches(seed):
     p, image = pkv.plan_host(lens, ql, hq, hkv, d, nq, window=window)
     assert p.window_left == window
     _check_plan(p, image, lens, ql, hq, hkv, window)
+    # tail queues (one per decode queue, the last prefill queues) exactly
+    # when the step has decode units and chunk units
+    decode_units = int(p.num_units) - int(p.num_prefill_units)
+    tails = nq if decode_units > 0 and int(p.num_prefill_units) > 0 else 0
+    assert int(p.num_tail_queues) == tails
+    if tails:
+        assert int(p.num_prefill_queues) == 2 * nq
 
     # the same batch at a capacity: same content at the capacity's offsets
     cap_seqs = lens.shape[0] + int(rng.integers(0, 8))
