@@ -629,6 +629,13 @@ constexpr int kRingStages = 4;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Cache policy field of a direct-to-LDS load: the default one (the ring's
+// tiles, whose keys the other row blocks of a chunk read again), or
+// non-temporal (the nt bit on gfx950), as the decode unit's K/V loads are
+// (the few-row kernel's tiles, read once).
+constexpr int kLdsLoadDefault = 0;
+constexpr int kLdsLoadNt = 2;
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone; gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -709,7 +716,7 @@ __device__ __forceinline__ void prefill_queue_ring(const AttnArgs& a, int queue,
                 for (int e = 0; e < SE; ++e)
                     __builtin_amdgcn_global_load_lds(src + e * slot_src_step,
                                                      (lds_void_t*)(st + (8 * f + wave + NWV * e) * kRingSlotElems),
-                                                     16, 0, 0);
+                                                     16, 0, kLdsLoadDefault);
             }
         };
 
@@ -820,18 +827,18 @@ void prefill_wide_kernel(AttnArgs a, int queue0) {
 // block) and every kv head.  One 8-wave workgroup per queue; wave w takes kv
 // heads w, w + 8, ... of each unit, so that the workgroup streams whole key
 // rows of the pool as the decode kernel does.  A wave walks the unit's
-// 32-key tiles on its own, with no barrier: it loads a tile's K and V rows
-// into registers (each load instruction two whole 256-byte rows of K and
-// two of V), writes them to an LDS tile of its own in the ring layout and
-// reads the operands back as the ring path does.  One tile is in flight per
-// wave (two measured slower: the read rate of the pool falls with more bytes
-// in flight per CU, as for the decode kernel): for fp8 codes the next tile's
-// loads go out once the current tile is in LDS, before its products (their
-// widening then overlaps the loads); for bf16 after the products (1 % faster
-// on a speculative verify step).  All loads go
-// to registers, so the compiler's waits for them count exactly.  bf16 K/V,
-// D = 128, pages of a power of two >= 16 tokens (each 16-key half of a tile
-// lies in one page).
+// 32-key tiles on its own, with no barrier, through an LDS tile of its own in
+// the ring layout (each load instruction two whole 256-byte rows of K and
+// two of V), reading the operands back as the ring path does.  bf16 rows go
+// straight to the LDS tile (direct-to-LDS, non-temporal), and the next
+// tile's loads go out once the tile's products have read it, so that no
+// load is in flight while the wave reads LDS.  fp8 codes go to registers
+// and are widened to bf16 as they are written to the tile; there the next
+// tile's loads go out before the products, which overlap them.  One tile is
+// in flight per wave (two measured slower: the read rate of the pool falls
+// with more bytes in flight per CU, as for the decode kernel).  D = 128,
+// pages of a power of two >= 16 tokens (each 16-key half of a tile lies in
+// one page).
 // ---------------------------------------------------------------------------
 constexpr int kFrWaves = 8;
 
@@ -884,72 +891,106 @@ __device__ __forceinline__ void fewrow_head(const AttnArgs& a, const Unit& un, i
     const int ntiles = kend > kb ? (kend - kb + kPfKeys - 1) / kPfKeys : 0;
     const int glast = kend > kb ? ((kend - 1) & ~15) : kb;  // start of the unit's last 16 keys
 
-    // Loads of tile i into r: per half f of 16 keys (clamped to the unit's
-    // last half, so that every address lies in a page of the sequence or in
-    // the pool's first page) its page-table entry and one load per slot.
-    // Past the unit's last tile (the loop issues one tile ahead whether or
-    // not there is one, so that the compiler counts the loads in flight
-    // exactly at every wait) they read the first rows of the pool (a few
-    // KiB, cached) and are never used.
-    auto issue = [&](int i, Regs& r) {
-        const int t0 = kb + kPfKeys * i;
-        const bool live = i < ntiles;
+    if constexpr (KVDT == PKV_DTYPE_BF16) {
+        // bf16: tile i straight into the wave's LDS tile, per half f of 16
+        // keys (clamped to the unit's last half, so that every address lies
+        // in a page of the sequence or in the pool's first page) its
+        // page-table entry and one direct-to-LDS load per slot.  Only the
+        // wave reads its tile, so a vmcnt wait publishes it; the next tile's
+        // loads go out once the tile's products have read it.
+        auto issue = [&](int i) {
+            const int t0 = kb + kPfKeys * i;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const int g = min(t0 + 16 * f, glast);
-            const int pidx = g >> shift;
-            const int32_t e = tbl.clamped(pidx);
-            const bool ok = pidx < tbl.n && static_cast<uint32_t>(e) < nblocks;
-            W.bad |= t0 + 16 * f < kend && !ok;
-            // fp8 codes: the page id times the page's bytes plus the row's
-            // offset (fewer scalar instructions: measured faster there, not
-            // for bf16)
-            const char* base;
-            if constexpr (KVDT == PKV_DTYPE_FP8_E4M3) {
-                base = live ? head_src + static_cast<uint64_t>(static_cast<uint32_t>(ok ? e : 0)) * page_bytes +
-                                  static_cast<uint64_t>(static_cast<uint32_t>(g - (pidx << shift))) * row_bytes
-                            : head_src;
-            } else {
-                const int64_t row0 =
-                    live ? static_cast<int64_t>(ok ? e : 0) * a.block_size + (g - (pidx << shift)) : 0;
-                base = src + (row0 * a.hkv + h) * RB;
+            for (int f = 0; f < 2; ++f) {
+                const int g = min(t0 + 16 * f, glast);
+                const int pidx = g >> shift;
+                const int32_t e = tbl.clamped(pidx);
+                const bool ok = pidx < tbl.n && static_cast<uint32_t>(e) < nblocks;
+                W.bad |= t0 + 16 * f < kend && !ok;
+                const int64_t row0 = static_cast<int64_t>(ok ? e : 0) * a.block_size + (g - (pidx << shift));
+                const char* const base = src + (row0 * a.hkv + h) * RB;
+#pragma unroll
+                for (int i8 = 0; i8 < 8; ++i8)
+                    __builtin_amdgcn_global_load_lds(base + i8 * row_bytes,
+                                                     (lds_void_t*)(st + (8 * f + i8) * kRingSlotElems), 16, 0,
+                                                     kLdsLoadNt);
+            }
+        };
+        if (ntiles > 0) issue(0);
+        for (int c = 0; c < ntiles; ++c) {
+            const int t0 = kb + kPfKeys * c;
+            wait_vmcnt<0>();
+            // V rows of keys at or past kend were read from inside their
+            // page (or from the last half): zeros, so that a zero weight
+            // never meets a non-finite value
+            if (t0 + kPfKeys > kend) {
+                if (j >= 2) {
+#pragma unroll
+                    for (int s16 = 0; s16 < 16; ++s16)
+                        if (t0 + 16 * (s16 >> 3) + (s16 & 7) + 8 * (j & 1) >= kend)
+                            *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) =
+                                u32x4_t{0u, 0u, 0u, 0u};
+                }
+                wait_lgkmcnt0();
+            }
+            W.template tile<D / 32>(a, RingTile{st}, t0);
+            __asm__ volatile("" ::: "memory");  // the tile's reads stay before the loads that overwrite it
+            if (c + 1 < ntiles) issue(c + 1);
+        }
+    } else {
+        // fp8 codes: tile i into registers r, widened to bf16 as they are
+        // written to the LDS tile.  Per half f of 16 keys (clamped as above)
+        // its page-table entry and one load per slot.  Past the unit's last
+        // tile (the loop issues one tile ahead whether or not there is one,
+        // so that the compiler counts the loads in flight exactly at every
+        // wait) they read the first rows of the pool (a few KiB, cached) and
+        // are never used.
+        auto issue = [&](int i, Regs& r) {
+            const int t0 = kb + kPfKeys * i;
+            const bool live = i < ntiles;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const int g = min(t0 + 16 * f, glast);
+                const int pidx = g >> shift;
+                const int32_t e = tbl.clamped(pidx);
+                const bool ok = pidx < tbl.n && static_cast<uint32_t>(e) < nblocks;
+                W.bad |= t0 + 16 * f < kend && !ok;
+                // the page id times the page's bytes plus the row's offset
+                const char* const base =
+                    live ? head_src + static_cast<uint64_t>(static_cast<uint32_t>(ok ? e : 0)) * page_bytes +
+                               static_cast<uint64_t>(static_cast<uint32_t>(g - (pidx << shift))) * row_bytes
+                         : head_src;
+#pragma unroll
+                for (int i8 = 0; i8 < 8; ++i8)
+                    r.x[8 * f + i8] = __builtin_nontemporal_load(
+                        reinterpret_cast<const typename Regs::piece_t*>(base + i8 * row_bytes));
+            }
+        };
+        // tile c into the wave's LDS tile, V rows of keys at or past kend
+        // as zeros (the previous tile's reads of the LDS tile have
+        // completed: they are waited for where they are issued)
+        auto stage = [&](int c, const Regs& r) {
+            const int t0 = kb + kPfKeys * c;
+            if (t0 + kPfKeys <= kend) {  // every key of the tile is in the unit (uniform)
+#pragma unroll
+                for (int s16 = 0; s16 < 16; ++s16)
+                    *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) = fr_bf16(r.x[s16]);
+                return;
             }
 #pragma unroll
-            for (int i8 = 0; i8 < 8; ++i8)
-                r.x[8 * f + i8] = __builtin_nontemporal_load(
-                    reinterpret_cast<const typename Regs::piece_t*>(base + i8 * row_bytes));
-        }
-    };
-    // tile c into the wave's LDS tile; V rows of keys at or past kend were
-    // read from inside their page (or from the last half) and are stored as
-    // zeros, so that a zero weight never meets a non-finite value (the
-    // previous tile's reads of the LDS tile have completed: they are waited
-    // for where they are issued)
-    auto stage = [&](int c, const Regs& r) {
-        const int t0 = kb + kPfKeys * c;
-        if (t0 + kPfKeys <= kend) {  // every key of the tile is in the unit (uniform)
-#pragma unroll
-            for (int s16 = 0; s16 < 16; ++s16)
-                *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) = fr_bf16(r.x[s16]);
-            return;
-        }
-#pragma unroll
-        for (int s16 = 0; s16 < 16; ++s16) {
-            const bool zero = j >= 2 && t0 + 16 * (s16 >> 3) + (s16 & 7) + 8 * (j & 1) >= kend;
-            *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) =
-                zero ? u32x4_t{0u, 0u, 0u, 0u} : fr_bf16(r.x[s16]);
-        }
-    };
-
-    // one register set: a tile's registers are free once it is in LDS
-    Regs r;
-    issue(0, r);
-    for (int c = 0; c < ntiles; ++c) {
-        stage(c, r);
-        if constexpr (KVDT == PKV_DTYPE_BF16) {
-            W.template tile<D / 32>(a, RingTile{st}, kb + kPfKeys * c);
-            issue(c + 1, r);
-        } else {
+            for (int s16 = 0; s16 < 16; ++s16) {
+                const bool zero = j >= 2 && t0 + 16 * (s16 >> 3) + (s16 & 7) + 8 * (j & 1) >= kend;
+                *reinterpret_cast<u32x4_t*>(st + s16 * kRingSlotElems + lane * 8) =
+                    zero ? u32x4_t{0u, 0u, 0u, 0u} : fr_bf16(r.x[s16]);
+            }
+        };
+        // one register set: a tile's registers are free once it is in LDS;
+        // the next tile's loads go out before the tile's products, whose
+        // widening then overlaps them
+        Regs r;
+        issue(0, r);
+        for (int c = 0; c < ntiles; ++c) {
+            stage(c, r);
             issue(c + 1, r);
             W.template tile<D / 32>(a, RingTile{st}, kb + kPfKeys * c);
         }
